@@ -1,0 +1,252 @@
+"""Benchmark of the owner-side Gram Newton-Schulz Muon step on one MI355X.
+
+Default workload: one 4096-hidden decoder layer (Q, K, V, O 4096x4096; gate, up
+4096x11008; down 11008x4096), bf16, seeded N(0, 1e-3^2) gradients and momenta, 5 quintic
+iterations, lr 0.02, beta 0.95.  One step = one muon_step over all seven matrices
+(momentum, normalisation, Gram Newton-Schulz and the update), inputs resident in HBM.
+
+Prints one JSON line:
+  value          algorithmic TFLOP/s of the whole step (symmetric products count m(m+1)k)
+  roofline       the MFMA contraction kernel against the bf16 dense peak, its duration taken
+                 from HIP events around each of its launches over the timed steps
+  cpu_baseline   the float64 CPU oracle on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       python bench.py --copy-calibration BYTES   (plain copy kernel, for HBM counters)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "Muon NS step TFLOP/s + matrices/s, % of bf16 MFMA peak (1 GPU)"
+BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 flop/clk/CU
+F32_PEAK_TFLOPS = 157.3      # MI355X dense fp32 matrix
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+KERNEL_SOURCES = ["newton_schulz_02_amd/csrc/kernels_gemm.hip",
+                  "newton_schulz_02_amd/csrc/muon_internal.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        h.update((ROOT / rel).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch of the contraction kernel from the committed counter summary.
+
+    The summary records the kernel source hash it was taken with; a different hash means
+    the kernel changed since, and the figure is withheld (None).
+    """
+    path = ROOT / "profiles" / f"gemm_bf16_{workload}_hbm_traffic.md"
+    if not path.exists():
+        return None
+    text = path.read_text()
+    m_hash = re.search(r"kernel_hash:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(wl, budget_s: float = 30.0):
+    """Time the CPU oracle on a bounded sample of the workload: its matrices in list order
+    until about ``budget_s`` seconds have been spent (at least one matrix)."""
+    import numpy as np
+    import torch
+
+    from newton_schulz_02_amd import workloads as W
+    from oracle import muon_step as oracle_step
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((d.get("num_threads", 1) for d in threadpool_info()
+                       if d.get("user_api") == "blas"), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    done, flops, spent = [], 0.0, 0.0
+    for spec, w, g, m in W.generate(wl, weights="random"):
+        if done and spent >= budget_s * 0.5:
+            break
+        w64, g64, m64 = (t.to(torch.float64).numpy() for t in (w, g, m))
+        t0 = time.perf_counter()
+        oracle_step(w64, g64, m64, lr=wl.lr, beta=wl.beta, coeffs=wl.coeffs, steps=wl.steps, eps=wl.eps)
+        spent += time.perf_counter() - t0
+        mm, nn = min(spec.rows, spec.cols), max(spec.rows, spec.cols)
+        flops += algorithmic_flops_one(mm, nn, wl)
+        done.append(f"{spec.name} {spec.rows}x{spec.cols}")
+        if spent >= budget_s:
+            break
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"float64 direct Newton-Schulz oracle on {len(done)} of {wl.count} matrices "
+                  f"({', '.join(done)}), {spent:.1f} s; flops counted with the same rule as value",
+        "seconds": spent,
+    }
+
+
+def algorithmic_flops_one(m: int, n: int, wl) -> float:
+    import newton_schulz_02_amd as nm
+
+    arr = nm.shape_array([(m, n)])
+    hp = nm.make_hparams(lr=wl.lr, beta=wl.beta, coeffs=wl.coeffs, steps=wl.steps, eps=wl.eps)
+    return nm.step_cost(arr, 1, hp)[0]
+
+
+def copy_calibration(nbytes: int) -> None:
+    """A plain device copy of nbytes (read nbytes, write nbytes), for scaling HBM counters."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="layer4096_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=30.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the owner-side step needs no collective and "
+              "this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return 0
+
+    import torch
+
+    import newton_schulz_02_amd as nm
+    from newton_schulz_02_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    print(f"[bench] workload {wl.name}: {wl.count} matrices; drawing inputs", file=sys.stderr, flush=True)
+    params, grads, moms = [], [], []
+    for spec, w, g, m in W.generate(wl, weights="random", device=dev):
+        params.append(w)
+        grads.append(g)
+        moms.append(m)
+    tail = W.generate_tail(wl, device=dev)
+    step = nm.MuonStep(params, grads, moms, lr=wl.lr, beta=wl.beta, coeffs=wl.coeffs,
+                       steps=wl.steps, eps=wl.eps)
+    flops, ew_bytes = step.cost()
+    stream = torch.cuda.current_stream(dev)
+
+    def one_step():
+        step(stream)
+        if tail is not None:
+            t = wl.tail
+            nm.adamw_step(*tail, lr=t.lr, beta1=t.beta1, beta2=t.beta2, eps=t.eps,
+                          weight_decay=t.weight_decay, step=t.step, stream=stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    # Timed region: per-launch HIP events (on the launch stream) give the kernel durations.
+    nm.profile_begin()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    stats = nm.profile_end()
+    ms = start.elapsed_time(stop) / args.steps
+
+    value = flops / (ms * 1e-3) / 1e12
+    gemm_name = "gemm_bf16" if "gemm_bf16" in stats else "gemm_f32"
+    gs = stats[gemm_name]
+    peak = BF16_PEAK_TFLOPS if gemm_name == "gemm_bf16" else F32_PEAK_TFLOPS
+    avg_ms = gs["ms"] / gs["launches"]
+    flops_per_launch = gs["flops"] / gs["launches"]
+    achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
+    traffic = traffic_from_profiles(wl.name)
+    kernels = {k: {"launches": v["launches"] // args.steps, "ms_per_step": v["ms"] / args.steps,
+                   "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None,
+                   "gbs": (v["bytes"] / (v["ms"] * 1e-3) / 1e9) if v["bytes"] else None}
+               for k, v in stats.items()}
+    print(f"[bench] {ms:.3f} ms/step; per kernel: {json.dumps(kernels)}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, args.cpu_budget)
+
+    dtypes = sorted({s.dtype for s in wl.matrices})
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "+".join(dtypes),
+        "data": "synthetic",
+        "matrices_per_s": round(wl.count / (ms * 1e-3), 2),
+        "pct_of_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
+        "algorithmic_flops_per_step": flops,
+        "config": {
+            "workload": wl.name,
+            "matrices": wl.count,
+            "shapes": sorted({f"{s.rows}x{s.cols}" for s in wl.matrices}),
+            "ns_steps": wl.steps,
+            "coeffs": list(wl.coeffs),
+            "adamw_tail": wl.tail.numel if wl.tail else 0,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": gemm_name,
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "launches_per_step": gs["launches"] // args.steps,
+            "avg_launch_ms": round(avg_ms, 5),
+            "flops_per_launch": flops_per_launch,
+        },
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

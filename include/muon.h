@@ -1,0 +1,153 @@
+/*
+ * muon.h - C ABI of the owner-side Gram Newton-Schulz Muon step on one gfx950 GPU.
+ *
+ * What is computed (per owned weight matrix W of shape rows x cols):
+ *   1. momentum accumulation   M <- beta*M + G            (heavy-ball; DMuon summary §1,
+ *                                                          "momentum-aggregated gradients")
+ *   2. orientation             X = M if rows <= cols, else M^T, so X is m x n, m <= n
+ *                                                         (DMuon summary §2.2: the Gram
+ *                                                          saving holds for m < n)
+ *   3. Frobenius normalisation X0 = X / (||X||_F + eps)
+ *   4. Newton-Schulz, ns_steps iterations of X <- aX + b(XX^T)X + c(XX^T)^2X, evaluated in
+ *      the m x m Gram space G = X X^T (DMuon summary §2.2): P = aI + bG + cG^2,
+ *      G <- P G P, Q <- P Q, output O = Q X0.  Only the lower triangle of every symmetric
+ *      product is computed (DMuon summary §2.2, symmetric SYRK-type path) and mirrored on
+ *      store.  Same-shape matrices are batched into shared launches (DMuon summary §2.2,
+ *      batching).
+ *   5. update                  W <- W - lr * sqrt(max(1, rows/cols)) * O
+ *   The owner runs this once per matrix with no communication (DMuon summary §2.1;
+ *   MatrixFSDP summary, Methodology §1).  The 1D tail uses AdamW (MatrixFSDP summary,
+ *   Methodology §1) through adamw_step().
+ *
+ * Precision: bf16 matrices run bf16 MFMA products with fp32 accumulation and bf16 storage
+ * of every m x m iterate (round to nearest even); fp32 matrices run fp32 MFMA products
+ * with fp32 storage.  Elementwise math is fp32.
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers on the current HIP device.  Matrices are
+ *     row-major and contiguous (leading dimension = cols).
+ *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream) and the
+ *     call returns before it completes.  Buffers must stay valid and untouched until the
+ *     stream has reached that point.
+ *   - Every argument is validated on the host before the first HIP call; a validation
+ *     failure returns a negative status and enqueues nothing.
+ *   - No C++ exception crosses the ABI.  Status codes are muon_status values.
+ *   - The library allocates no device memory.  It keeps a small pinned host staging ring
+ *     for launch descriptors, released by muon_shutdown().
+ */
+#ifndef MUON_H
+#define MUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum muon_status {
+  MUON_OK = 0,
+  MUON_EINVAL = -1,      /* null pointer, bad size, unknown dtype, non-finite hyperparameter */
+  MUON_ENOSPC = -2,      /* workspace smaller than muon_workspace_size() */
+  MUON_EALIAS = -3,      /* grad overlaps an output (param/momentum) of any matrix, or
+                            outputs of two matrices overlap */
+  MUON_EHIP = -4,        /* a HIP runtime call failed; muon_last_error() has the text */
+  MUON_EUNSUPPORTED = -5 /* valid request this build cannot run (e.g. no gfx950 device) */
+} muon_status;
+
+typedef enum muon_dtype { MUON_BF16 = 1, MUON_F32 = 2 } muon_dtype;
+
+/* One owned matrix.  param and momentum are updated in place; grad is read only.
+ * All three have shape rows x cols, dtype `dtype`, row-major, contiguous. */
+typedef struct muon_matrix {
+  void* param;
+  const void* grad;
+  void* momentum;
+  int64_t rows;
+  int64_t cols;
+  int32_t dtype;    /* muon_dtype */
+  int32_t reserved; /* must be 0 */
+} muon_matrix;
+
+/* Restart set: bit k (1 <= k < ns_steps) re-anchors at the start of iteration k:
+ * X <- Q X, G <- X X^T, Q <- I.  Exact in real arithmetic (the result does not change);
+ * it bounds the bf16 error of the Gram iterate on near-square matrices.
+ * MUON_RESTART_AUTO picks, per matrix, {2, 3, ..., ns_steps-1} when n < 1.5 m (near-square:
+ * a restart costs no extra flops when m == n) and none otherwise. */
+#define MUON_RESTART_AUTO 0xFFFFFFFFu
+
+typedef struct muon_hparams {
+  float lr;       /* step size before the shape factor sqrt(max(1, rows/cols)) */
+  float beta;     /* momentum coefficient */
+  float ns_a;     /* Newton-Schulz polynomial a x + b x^3 + c x^5 */
+  float ns_b;
+  float ns_c;
+  int32_t ns_steps; /* 0..31; 0 gives O = X0 */
+  float eps;        /* added to ||X||_F before dividing; >= 0 */
+  uint32_t restart_mask;
+} muon_hparams;
+
+/* Bytes of device workspace muon_step() needs for this list.  Host only, no HIP call.
+ * Returns MUON_OK and writes *bytes, or MUON_EINVAL. */
+int muon_workspace_size(const muon_matrix* mats, int32_t count, const muon_hparams* hp,
+                        size_t* bytes);
+
+/* One Muon step over `count` owned matrices (count == 0 is a no-op).  `workspace` is a
+ * device buffer of at least muon_workspace_size() bytes, 256-byte aligned, owned by the
+ * caller and not touched by anything else until the stream passes this call; two calls
+ * in flight at once need two workspaces.  Matrices may mix dtypes. */
+int muon_step(const muon_matrix* mats, int32_t count, const muon_hparams* hp, void* workspace,
+              size_t workspace_bytes, void* hip_stream);
+
+/* AdamW on a packed fp32 vector of n values (MatrixFSDP summary, Methodology §1: the
+ * non-matrix tail keeps standard AdamW).  With t = step >= 1:
+ *   m <- b1 m + (1-b1) g;  v <- b2 v + (1-b2) g^2;
+ *   p <- p - lr * ( (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps) + weight_decay * p ).
+ * p, m, v are updated in place; g is read only; all device pointers, 4-byte aligned. */
+typedef struct adamw_hparams {
+  float lr;
+  float beta1;
+  float beta2;
+  float eps;
+  float weight_decay;
+  int32_t step;
+} adamw_hparams;
+
+int adamw_step(float* p, const float* g, float* m, float* v, int64_t n, const adamw_hparams* hp,
+               void* hip_stream);
+
+/* Algorithmic work of one muon_step over this list (host only): flops count a symmetric
+ * m x m x k product as m(m+1)k and a full product as 2*m*n*k; bytes count the compulsory
+ * HBM traffic of the elementwise phases.  Either output pointer may be NULL. */
+int muon_step_cost(const muon_matrix* mats, int32_t count, const muon_hparams* hp,
+                   double* flops, double* bytes);
+
+/* Host-side description of the launch plan (buckets, restart sets, launches) as a
+ * NUL-terminated JSON string written to buf (truncated to len).  Host only.  For tests. */
+int muon_plan_describe(const muon_matrix* mats, int32_t count, const muon_hparams* hp, char* buf,
+                       size_t len);
+
+/* Per-kernel timing.  Between muon_profile_begin() and muon_profile_end(), each launch made
+ * by muon_step()/adamw_step() is bracketed by HIP events on its stream.  muon_profile_end()
+ * waits for those events and writes one record per kernel kind. */
+typedef struct muon_kernel_stat {
+  char name[32];
+  int64_t launches;
+  double ms;     /* summed event time of those launches */
+  double flops;  /* algorithmic flops of those launches */
+  double bytes;  /* algorithmic bytes of those launches */
+} muon_kernel_stat;
+
+int muon_profile_begin(void);
+int muon_profile_end(muon_kernel_stat* out, int32_t max, int32_t* count);
+
+const char* muon_strerror(int status); /* static string */
+const char* muon_last_error(void);     /* detail of the last failure on this thread */
+const char* muon_version(void);
+void muon_shutdown(void);              /* frees the pinned staging ring; idempotent */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_H */

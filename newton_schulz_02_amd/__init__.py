@@ -1,0 +1,273 @@
+"""Python binding of libmuon, the owner-side Gram Newton-Schulz Muon step for gfx950.
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+``libmuon.so``.  PyTorch supplies device memory and the current stream.  If the library
+has not been built, every call raises ``MuonLibraryMissing``; there is no fallback.
+
+Entry points mirror ``include/muon.h``: :func:`workspace_size`, :func:`muon_step`,
+:func:`adamw_step`, :func:`step_cost`, :func:`plan_describe`, :func:`profile_begin`,
+:func:`profile_end`, :func:`strerror`, :func:`last_error`, :func:`version`,
+:func:`shutdown`.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import json
+from ctypes import POINTER, c_char, c_char_p, c_double, c_float, c_int, c_int32, c_int64, c_size_t, c_uint32, c_void_p
+from pathlib import Path
+
+LIB_PATH = Path(__file__).resolve().with_name("libmuon.so")
+
+MUON_OK = 0
+MUON_EINVAL = -1
+MUON_ENOSPC = -2
+MUON_EALIAS = -3
+MUON_EHIP = -4
+MUON_EUNSUPPORTED = -5
+MUON_BF16 = 1
+MUON_F32 = 2
+RESTART_AUTO = 0xFFFFFFFF
+
+#: Coefficients published with Muon (Jordan et al., 2024).  The pages print none.
+QUINTIC = (3.4445, -4.7750, 2.0315)
+
+
+class MuonLibraryMissing(RuntimeError):
+    pass
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{strerror(status)} ({status}): {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class muon_matrix(ctypes.Structure):
+    _fields_ = [("param", c_void_p), ("grad", c_void_p), ("momentum", c_void_p),
+                ("rows", c_int64), ("cols", c_int64), ("dtype", c_int32), ("reserved", c_int32)]
+
+
+class muon_hparams(ctypes.Structure):
+    _fields_ = [("lr", c_float), ("beta", c_float), ("ns_a", c_float), ("ns_b", c_float),
+                ("ns_c", c_float), ("ns_steps", c_int32), ("eps", c_float),
+                ("restart_mask", c_uint32)]
+
+
+class adamw_hparams(ctypes.Structure):
+    _fields_ = [("lr", c_float), ("beta1", c_float), ("beta2", c_float), ("eps", c_float),
+                ("weight_decay", c_float), ("step", c_int32)]
+
+
+class muon_kernel_stat(ctypes.Structure):
+    _fields_ = [("name", c_char * 32), ("launches", c_int64), ("ms", c_double),
+                ("flops", c_double), ("bytes", c_double)]
+
+
+_MATP = POINTER(muon_matrix)
+_HPP = POINTER(muon_hparams)
+_SIGNATURES = {
+    "muon_workspace_size": (c_int, [_MATP, c_int32, _HPP, POINTER(c_size_t)]),
+    "muon_step": (c_int, [_MATP, c_int32, _HPP, c_void_p, c_size_t, c_void_p]),
+    "adamw_step": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, POINTER(adamw_hparams), c_void_p]),
+    "muon_step_cost": (c_int, [_MATP, c_int32, _HPP, POINTER(c_double), POINTER(c_double)]),
+    "muon_plan_describe": (c_int, [_MATP, c_int32, _HPP, c_char_p, c_size_t]),
+    "muon_profile_begin": (c_int, []),
+    "muon_profile_end": (c_int, [POINTER(muon_kernel_stat), c_int32, POINTER(c_int32)]),
+    "muon_strerror": (c_char_p, [c_int]),
+    "muon_last_error": (c_char_p, []),
+    "muon_version": (c_char_p, []),
+    "muon_shutdown": (None, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmuon.so (once).  Raises MuonLibraryMissing if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise MuonLibraryMissing(
+                f"{LIB_PATH} not found: build it with `python -m newton_schulz_02_amd.build`")
+        handle = ctypes.CDLL(str(LIB_PATH))
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().muon_strerror(int(status)).decode()
+
+
+def last_error() -> str:
+    return lib().muon_last_error().decode()
+
+
+def version() -> str:
+    return lib().muon_version().decode()
+
+
+def shutdown() -> None:
+    lib().muon_shutdown()
+
+
+def _check(status: int) -> None:
+    if status != MUON_OK:
+        raise MuonError(status, last_error())
+
+
+# --- descriptors ------------------------------------------------------------------------
+
+def make_hparams(lr=0.02, beta=0.95, coeffs=QUINTIC, steps=5, eps=1e-7,
+                 restart_mask=RESTART_AUTO) -> muon_hparams:
+    a, b, c = coeffs
+    return muon_hparams(float(lr), float(beta), float(a), float(b), float(c), int(steps),
+                        float(eps), int(restart_mask) & 0xFFFFFFFF)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return MUON_BF16
+    if t.dtype == torch.float32:
+        return MUON_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def matrix_array(params, grads, moms):
+    """Pack lists of 2D device tensors into a ctypes muon_matrix array."""
+    if not (len(params) == len(grads) == len(moms)):
+        raise ValueError("params, grads and moms must have the same length")
+    arr = (muon_matrix * max(1, len(params)))()
+    for i, (w, g, m) in enumerate(zip(params, grads, moms)):
+        for t in (w, g, m):
+            if t.dim() != 2 or not t.is_contiguous():
+                raise ValueError(f"matrix {i}: tensors must be 2D and contiguous")
+            if tuple(t.shape) != tuple(w.shape) or t.dtype != w.dtype:
+                raise ValueError(f"matrix {i}: param, grad and momentum must match in shape and dtype")
+        arr[i] = muon_matrix(w.data_ptr(), g.data_ptr(), m.data_ptr(), w.shape[0], w.shape[1],
+                             _dtype_code(w), 0)
+    return arr
+
+
+def shape_array(shapes, dtype=MUON_BF16):
+    """A muon_matrix array with fake, distinct, aligned pointers: for host-only planning calls."""
+    arr = (muon_matrix * max(1, len(shapes)))()
+    base = 1 << 40
+    for i, sh in enumerate(shapes):
+        r, c = sh[0], sh[1]
+        dt = sh[2] if len(sh) > 2 else dtype
+        es = 2 if dt == MUON_BF16 else 4
+        nbytes = ((r * c * es + 4095) // 4096) * 4096
+        arr[i] = muon_matrix(base, base + nbytes, base + 2 * nbytes, r, c, dt, 0)
+        base += 3 * nbytes
+    return arr
+
+
+def _stream_handle(stream, device):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+# --- entry points -----------------------------------------------------------------------
+
+def workspace_size_raw(arr, count: int, hp: muon_hparams) -> int:
+    out = c_size_t(0)
+    _check(lib().muon_workspace_size(arr, int(count), ctypes.byref(hp), ctypes.byref(out)))
+    return int(out.value)
+
+
+def step_raw(arr, count: int, hp: muon_hparams, ws_ptr: int, ws_bytes: int, stream_ptr) -> None:
+    _check(lib().muon_step(arr, int(count), ctypes.byref(hp), c_void_p(ws_ptr), int(ws_bytes),
+                           stream_ptr))
+
+
+def workspace_size(params, grads, moms, **hp) -> int:
+    return workspace_size_raw(matrix_array(params, grads, moms), len(params), make_hparams(**hp))
+
+
+def step_cost(arr, count: int, hp: muon_hparams) -> tuple[float, float]:
+    f, b = c_double(0), c_double(0)
+    _check(lib().muon_step_cost(arr, int(count), ctypes.byref(hp), ctypes.byref(f), ctypes.byref(b)))
+    return f.value, b.value
+
+
+def plan_describe(arr, count: int, hp: muon_hparams, size: int = 1 << 24) -> dict:
+    buf = ctypes.create_string_buffer(size)
+    _check(lib().muon_plan_describe(arr, int(count), ctypes.byref(hp), buf, size))
+    return json.loads(buf.value.decode())
+
+
+class MuonStep:
+    """A prepared Muon step over fixed lists of device tensors.
+
+    Holds the packed descriptors and a torch-allocated workspace; each call enqueues one
+    ``muon_step`` on the current (or given) stream.
+    """
+
+    def __init__(self, params, grads, moms, *, lr=0.02, beta=0.95, coeffs=QUINTIC, steps=5,
+                 eps=1e-7, restart_mask=RESTART_AUTO, workspace=None):
+        import torch
+
+        self.params, self.grads, self.moms = list(params), list(grads), list(moms)
+        self.count = len(self.params)
+        self.hp = make_hparams(lr, beta, coeffs, steps, eps, restart_mask)
+        self.arr = matrix_array(self.params, self.grads, self.moms)
+        self.ws_bytes = workspace_size_raw(self.arr, self.count, self.hp)
+        self.device = self.params[0].device if self.count else torch.device("cuda")
+        if workspace is None:
+            workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
+        if workspace.numel() < self.ws_bytes:
+            raise ValueError(f"workspace has {workspace.numel()} bytes, needs {self.ws_bytes}")
+        self.workspace = workspace
+
+    def cost(self) -> tuple[float, float]:
+        return step_cost(self.arr, self.count, self.hp)
+
+    def __call__(self, stream=None) -> None:
+        step_raw(self.arr, self.count, self.hp, self.workspace.data_ptr(), self.workspace.numel(),
+                 _stream_handle(stream, self.device))
+
+
+def muon_step(params, grads, moms, *, stream=None, **hp) -> None:
+    """One Muon step over lists of device tensors (param and momentum updated in place)."""
+    MuonStep(params, grads, moms, **hp)(stream)
+
+
+def adamw_step(p, g, m, v, *, lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
+               step=1, stream=None) -> None:
+    """AdamW on packed fp32 device vectors (p, m, v updated in place)."""
+    import torch
+
+    for t in (p, g, m, v):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("adamw tensors must be contiguous float32")
+        if t.numel() != p.numel():
+            raise ValueError("adamw tensors must have the same size")
+    hp = adamw_hparams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step))
+    _check(lib().adamw_step(c_void_p(p.data_ptr()), c_void_p(g.data_ptr()), c_void_p(m.data_ptr()),
+                            c_void_p(v.data_ptr()), p.numel(), ctypes.byref(hp),
+                            _stream_handle(stream, p.device)))
+
+
+def profile_begin() -> None:
+    _check(lib().muon_profile_begin())
+
+
+def profile_end() -> dict:
+    """Stop per-launch timing and return {kernel: {launches, ms, flops, bytes}}."""
+    out = (muon_kernel_stat * 16)()
+    n = c_int32(0)
+    _check(lib().muon_profile_end(out, 16, ctypes.byref(n)))
+    return {out[i].name.decode(): {"launches": out[i].launches, "ms": out[i].ms,
+                                   "flops": out[i].flops, "bytes": out[i].bytes}
+            for i in range(min(n.value, 16))}

@@ -1,0 +1,76 @@
+"""Build ``libmuon.so`` (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
+
+Usage:  python -m newton_schulz_02_amd.build  [--verbose]
+
+Each source is compiled to an object under ``newton_schulz_02_amd/_build`` in parallel,
+then linked into ``newton_schulz_02_amd/libmuon.so``.  Packed-fp32 instruction
+generation is disabled for all device code.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+BUILD = PKG / "_build"
+LIB = PKG / "libmuon.so"
+ARCH = "gfx950"
+
+SOURCES = ["planner.cpp", "muon_api.cpp", "kernels_elementwise.hip", "kernels_gemm.hip"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and Path(cand).exists():
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def _compile(src: Path, obj: Path, verbose: bool) -> None:
+    cmd = [hipcc(), "-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{ROOT / 'include'}", f"-I{CSRC}"]
+    if src.suffix == ".hip":
+        cmd += ["-x", "hip", f"--offload-arch={ARCH}", *DEVICE_FLAGS]
+    else:
+        cmd += ["-D__HIP_PLATFORM_AMD__"]
+    cmd += ["-c", str(src), "-o", str(obj)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = (res.stdout + res.stderr).strip()
+    # hipcc's host pass warns that it does not know the packed-fp32 feature; drop that noise.
+    lines = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src.name}:\n" + "\n".join(lines))
+    if verbose and lines:
+        print("\n".join(lines), flush=True)
+
+
+def build(verbose: bool = False) -> Path:
+    BUILD.mkdir(exist_ok=True)
+    objs = [BUILD / (Path(s).stem + ".o") for s in SOURCES]
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        futs = [ex.submit(_compile, CSRC / s, o, verbose) for s, o in zip(SOURCES, objs)]
+        for f in futs:
+            f.result()
+    tmp = LIB.with_suffix(".so.tmp")
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", str(tmp), *map(str, objs)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    path = build(verbose="--verbose" in sys.argv)
+    print(path)

@@ -1,0 +1,401 @@
+// C ABI of libmuon: argument validation, planning, descriptor upload and the launch
+// sequence of one owner-side Muon step (DMuon summary §2.1: the owner computes each
+// update once; §2.2: Gram Newton-Schulz with the symmetric path and shape batching).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/muon.h"
+#include "muon_internal.h"
+#include "planner.h"
+
+using namespace muon;
+
+namespace {
+
+thread_local std::string t_last_error;
+
+int fail(int status, const std::string& msg) {
+  t_last_error = msg;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  t_last_error = std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
+  return MUON_EHIP;
+}
+
+std::mutex g_mu;
+
+// Pinned host staging for descriptor uploads: a ring of slots per device, each guarded by
+// an event so a slot is rewritten only after its previous copy has left host memory.
+struct Slot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool used = false;
+};
+struct DeviceState {
+  bool checked = false;
+  bool supported = false;
+  Slot ring[4];
+  int next = 0;
+};
+std::map<int, DeviceState> g_dev;
+
+// Profiling records.
+struct Rec {
+  std::string name;
+  int device;
+  hipEvent_t a, b;
+  double flops, bytes;
+};
+bool g_prof = false;
+std::vector<Rec> g_recs;
+std::map<int, std::vector<hipEvent_t>> g_event_pool;
+
+int current_device(int* dev) {
+  hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  return MUON_OK;
+}
+
+// Caller holds g_mu.
+int check_device(int dev) {
+  DeviceState& st = g_dev[dev];
+  if (!st.checked) {
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    st.supported = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    st.checked = true;
+    if (!st.supported)
+      t_last_error = std::string("device architecture ") + prop.gcnArchName + " is not gfx950";
+  }
+  return st.supported ? MUON_OK : fail(MUON_EUNSUPPORTED, t_last_error);
+}
+
+// Caller holds g_mu.
+int upload(int dev, const void* src, size_t bytes, void* dst, hipStream_t s) {
+  DeviceState& st = g_dev[dev];
+  Slot& sl = st.ring[st.next];
+  st.next = (st.next + 1) % 4;
+  hipError_t e;
+  if (!sl.ev) {
+    e = hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+  }
+  if (sl.used) {
+    e = hipEventSynchronize(sl.ev);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (staging)");
+  }
+  if (sl.cap < bytes) {
+    if (sl.host) hipHostFree(sl.host);
+    sl.host = nullptr;
+    sl.cap = 0;
+    size_t cap = 4096;
+    while (cap < bytes) cap *= 2;
+    e = hipHostMalloc(&sl.host, cap, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc (staging)");
+    sl.cap = cap;
+  }
+  std::memcpy(sl.host, src, bytes);
+  e = hipMemcpyAsync(dst, sl.host, bytes, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (descriptors)");
+  e = hipEventRecord(sl.ev, s);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord (staging)");
+  sl.used = true;
+  return MUON_OK;
+}
+
+// Caller holds g_mu.
+hipEvent_t take_event(int dev) {
+  auto& pool = g_event_pool[dev];
+  if (!pool.empty()) {
+    hipEvent_t e = pool.back();
+    pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Run one launch, bracketed by timing events when profiling.  Caller holds g_mu.
+template <typename F>
+int timed(int dev, hipStream_t s, const char* name, double flops, double bytes, F&& launch) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (g_prof) {
+    a = take_event(dev);
+    b = take_event(dev);
+    if (!a || !b) return fail(MUON_EHIP, "hipEventCreate (profiling)");
+    const hipError_t e = hipEventRecord(a, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord (profiling)");
+  }
+  const int e = launch();
+  if (e != hipSuccess) return hip_fail(hipError_t(e), name);
+  if (g_prof) {
+    const hipError_t eb = hipEventRecord(b, s);
+    if (eb != hipSuccess) return hip_fail(eb, "hipEventRecord (profiling)");
+    g_recs.push_back({name, dev, a, b, flops, bytes});
+  }
+  return MUON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* muon_version(void) { return "muon-gfx950 0.1.0"; }
+
+const char* muon_strerror(int status) {
+  switch (status) {
+    case MUON_OK: return "success";
+    case MUON_EINVAL: return "invalid argument";
+    case MUON_ENOSPC: return "workspace too small";
+    case MUON_EALIAS: return "overlapping buffers";
+    case MUON_EHIP: return "HIP runtime error";
+    case MUON_EUNSUPPORTED: return "unsupported device or request";
+    default: return "unknown status";
+  }
+}
+
+const char* muon_last_error(void) { return t_last_error.c_str(); }
+
+int muon_workspace_size(const muon_matrix* mats, int32_t count, const muon_hparams* hp,
+                        size_t* bytes) {
+  try {
+    if (!bytes) return fail(MUON_EINVAL, "bytes is NULL");
+    Plan plan;
+    std::string err;
+    const int rc = build_plan(mats, count, hp, &plan, &err);
+    if (rc != MUON_OK) return fail(rc, err);
+    *bytes = count > 0 ? plan.ws_bytes : 0;
+    return MUON_OK;
+  } catch (const std::exception& e) {
+    return fail(MUON_EINVAL, e.what());
+  }
+}
+
+int muon_step_cost(const muon_matrix* mats, int32_t count, const muon_hparams* hp, double* flops,
+                   double* bytes) {
+  try {
+    Plan plan;
+    std::string err;
+    const int rc = build_plan(mats, count, hp, &plan, &err);
+    if (rc != MUON_OK) return fail(rc, err);
+    if (flops) *flops = plan.flops;
+    if (bytes) *bytes = plan.bytes;
+    return MUON_OK;
+  } catch (const std::exception& e) {
+    return fail(MUON_EINVAL, e.what());
+  }
+}
+
+int muon_plan_describe(const muon_matrix* mats, int32_t count, const muon_hparams* hp, char* buf,
+                       size_t len) {
+  try {
+    if (!buf || len == 0) return fail(MUON_EINVAL, "buf is NULL or empty");
+    Plan plan;
+    std::string err;
+    const int rc = build_plan(mats, count, hp, &plan, &err);
+    if (rc != MUON_OK) return fail(rc, err);
+    const std::string s = describe_plan(plan);
+    const size_t n = std::min(len - 1, s.size());
+    std::memcpy(buf, s.data(), n);
+    buf[n] = '\0';
+    if (s.size() >= len) return fail(MUON_ENOSPC, "description truncated");
+    return MUON_OK;
+  } catch (const std::exception& e) {
+    return fail(MUON_EINVAL, e.what());
+  }
+}
+
+int muon_step(const muon_matrix* mats, int32_t count, const muon_hparams* hp, void* workspace,
+              size_t workspace_bytes, void* hip_stream) {
+  try {
+    Plan plan;
+    std::string err;
+    int rc = build_plan(mats, count, hp, &plan, &err);
+    if (rc != MUON_OK) return fail(rc, err);
+    if (count == 0) return MUON_OK;
+    if (!workspace) return fail(MUON_EINVAL, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(MUON_EINVAL, "workspace is not 256-byte aligned");
+    if (workspace_bytes < plan.ws_bytes) {
+      char buf[128];
+      snprintf(buf, sizeof buf, "workspace has %zu bytes, needs %zu", workspace_bytes,
+               plan.ws_bytes);
+      return fail(MUON_ENOSPC, buf);
+    }
+    char* ws = static_cast<char*>(workspace);
+    std::vector<MatDesc> descs;
+    fill_descs(plan, mats, hp, ws, &descs);
+
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0;
+    if ((rc = current_device(&dev)) != MUON_OK) return rc;
+    if ((rc = check_device(dev)) != MUON_OK) return rc;
+    if ((rc = upload(dev, descs.data(), descs.size() * sizeof(MatDesc), ws + plan.desc_off, s)) !=
+        MUON_OK)
+      return rc;
+
+    const MatDesc* ddesc = reinterpret_cast<const MatDesc*>(ws + plan.desc_off);
+    float* scale = reinterpret_cast<float*>(ws + plan.scale_off);
+    float* partials = reinterpret_cast<float*>(ws + plan.partial_off);
+    for (const PlanLaunch& L : plan.launches) {
+      if (L.kind == kLaunchMomentum) {
+        MomArgs a;
+        a.desc = ddesc;
+        a.partials = partials;
+        a.first = L.first;
+        a.last = L.last;
+        a.tile_begin = int32_t(plan.mats[L.first].mom_prefix);
+        a.total_tiles = int32_t(L.tiles);
+        a.beta = hp->beta;
+        rc = timed(dev, s, L.dtype == kBF16 ? "momentum_bf16" : "momentum_f32", 0.0, L.bytes,
+                   [&] { return muon_launch_momentum(a, L.dtype, s); });
+      } else if (L.kind == kLaunchNorm) {
+        NormArgs a;
+        a.desc = ddesc;
+        a.partials = partials;
+        a.scale = scale;
+        a.count = count;
+        a.eps = hp->eps;
+        rc = timed(dev, s, "norm", 0.0, 0.0, [&] { return muon_launch_norm(a, s); });
+      } else {
+        GemmArgs a;
+        std::memset(&a, 0, sizeof a);
+        a.desc = ddesc;
+        a.scale = scale;
+        a.pa = hp->ns_a;
+        a.pb = hp->ns_b;
+        a.pc = hp->ns_c;
+        a.ngroups = int32_t(L.groups.size());
+        a.total_tiles = int32_t(L.tiles);
+        for (size_t g = 0; g < L.groups.size(); ++g) a.g[g] = L.groups[g];
+        rc = timed(dev, s, L.dtype == kBF16 ? "gemm_bf16" : "gemm_f32", L.flops, 0.0,
+                   [&] { return muon_launch_gemm(a, L.dtype, s); });
+      }
+      if (rc != MUON_OK) return rc;
+    }
+    return MUON_OK;
+  } catch (const std::exception& e) {
+    return fail(MUON_EHIP, std::string("exception: ") + e.what());
+  }
+}
+
+int adamw_step(float* p, const float* g, float* m, float* v, int64_t n, const adamw_hparams* hp,
+               void* hip_stream) {
+  try {
+    if (!hp) return fail(MUON_EINVAL, "hparams is NULL");
+    if (n < 0) return fail(MUON_EINVAL, "n is negative");
+    const float fs[] = {hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
+    for (float f : fs)
+      if (!std::isfinite(f)) return fail(MUON_EINVAL, "non-finite hyperparameter");
+    if (hp->step < 1) return fail(MUON_EINVAL, "step must be >= 1");
+    if (hp->beta1 < 0.0f || hp->beta1 >= 1.0f || hp->beta2 < 0.0f || hp->beta2 >= 1.0f)
+      return fail(MUON_EINVAL, "beta1/beta2 outside [0, 1)");
+    if (n == 0) return MUON_OK;
+    if (!p || !g || !m || !v) return fail(MUON_EINVAL, "NULL pointer");
+    const uintptr_t ptrs[4] = {(uintptr_t)p, (uintptr_t)g, (uintptr_t)m, (uintptr_t)v};
+    for (uintptr_t x : ptrs)
+      if (x % 4) return fail(MUON_EINVAL, "pointer not 4-byte aligned");
+    const uintptr_t bytes = uintptr_t(n) * 4;
+    for (int i = 0; i < 4; ++i)
+      for (int j = i + 1; j < 4; ++j)
+        if (ptrs[i] < ptrs[j] + bytes && ptrs[j] < ptrs[i] + bytes)
+          return fail(MUON_EALIAS, "AdamW buffers overlap");
+    AdamArgs a;
+    a.p = p;
+    a.g = g;
+    a.m = m;
+    a.v = v;
+    a.n = n;
+    a.lr = hp->lr;
+    a.beta1 = hp->beta1;
+    a.beta2 = hp->beta2;
+    a.eps = hp->eps;
+    a.wd = hp->weight_decay;
+    a.bc1 = float(1.0 - std::pow(double(hp->beta1), double(hp->step)));
+    a.bc2 = float(1.0 - std::pow(double(hp->beta2), double(hp->step)));
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0, rc;
+    if ((rc = current_device(&dev)) != MUON_OK) return rc;
+    if ((rc = check_device(dev)) != MUON_OK) return rc;
+    return timed(dev, s, "adamw", 0.0, 28.0 * double(n), [&] { return muon_launch_adamw(a, s); });
+  } catch (const std::exception& e) {
+    return fail(MUON_EHIP, std::string("exception: ") + e.what());
+  }
+}
+
+int muon_profile_begin(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_prof = true;
+  return MUON_OK;
+}
+
+int muon_profile_end(muon_kernel_stat* out, int32_t max, int32_t* count) {
+  try {
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_prof = false;
+    std::vector<muon_kernel_stat> stats;
+    int rc = MUON_OK;
+    for (Rec& r : g_recs) {
+      float ms = 0.0f;
+      hipError_t e = hipEventSynchronize(r.b);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+      if (e != hipSuccess && rc == MUON_OK) rc = hip_fail(e, "hipEventElapsedTime");
+      muon_kernel_stat* st = nullptr;
+      for (auto& x : stats)
+        if (r.name == x.name) st = &x;
+      if (!st) {
+        muon_kernel_stat z;
+        std::memset(&z, 0, sizeof z);
+        std::snprintf(z.name, sizeof z.name, "%s", r.name.c_str());
+        stats.push_back(z);
+        st = &stats.back();
+      }
+      st->launches += 1;
+      st->ms += double(ms);
+      st->flops += r.flops;
+      st->bytes += r.bytes;
+      g_event_pool[r.device].push_back(r.a);
+      g_event_pool[r.device].push_back(r.b);
+    }
+    g_recs.clear();
+    const int32_t n = int32_t(stats.size());
+    if (count) *count = n;
+    if (out)
+      for (int32_t i = 0; i < n && i < max; ++i) out[i] = stats[size_t(i)];
+    return rc;
+  } catch (const std::exception& e) {
+    return fail(MUON_EHIP, std::string("exception: ") + e.what());
+  }
+}
+
+void muon_shutdown(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (auto& kv : g_dev) {
+    for (Slot& sl : kv.second.ring) {
+      if (sl.used && sl.ev) hipEventSynchronize(sl.ev);
+      if (sl.host) hipHostFree(sl.host);
+      if (sl.ev) hipEventDestroy(sl.ev);
+      sl = Slot();
+    }
+  }
+  for (auto& kv : g_event_pool)
+    for (hipEvent_t e : kv.second) hipEventDestroy(e);
+  g_event_pool.clear();
+  g_dev.clear();
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// Internal types shared by the host planner and the gfx950 kernels of libmuon.
+//
+// Data layout in HBM (all row-major):
+//   - caller buffers: W, G, M are rows x cols with leading dimension cols;
+//   - per matrix, m = min(rows, cols), n = max(rows, cols), mp = round_up(m, 64),
+//     np = round_up(n, 64);
+//   - Gram slots (5 per matrix): m rows x mp columns, columns m..mp-1 held at zero so a
+//     contraction may always run over mp;
+//   - row form X (m x np) and transposed form X^T (n x mp), zero padded the same way.
+//     When the caller's momentum buffer already has a 64-multiple leading dimension and
+//     16-byte alignment it is used in place as one of the two forms.
+#pragma once
+
+#include <cstdint>
+
+namespace muon {
+
+constexpr int kTile = 256;       // output tile edge of the MFMA kernels (both dtypes)
+constexpr int kKPad = 64;        // contraction dimensions are padded to this multiple
+constexpr int kEwTile = 64;      // tile edge of the momentum/transpose kernel
+constexpr int kMaxGroups = 8;    // op groups per grouped GEMM launch
+constexpr int kSlots = 5;        // m x m Gram buffers per matrix
+
+enum DType : int32_t { kBF16 = 1, kF32 = 2 };
+
+// Buffer ids inside MatDesc::buf.
+enum BufId : int8_t {
+  kSlot0 = 0,  // .. kSlot0 + kSlots - 1: Gram iterates G, P, Q, T
+  kXrIn = 5,   // initial row form X (m x n)
+  kXtIn = 6,   // initial transposed form X^T (n x m)
+  kXrWs = 7,   // re-anchored row form
+  kXtWs0 = 8,  // re-anchored transposed form, ping
+  kXtWs1 = 9,  // re-anchored transposed form, pong
+  kW = 10,     // the parameter (rows x cols), output of the update
+  kNumBuf = 11
+};
+
+// Epilogue / op kinds of the grouped GEMM.
+enum OpKind : int8_t {
+  kOpSyrk = 0,    // C = alpha * A A^T, lower tiles, mirrored
+  kOpPoly = 1,    // C = pa*I + pb*E + pc*(A B^T), lower tiles, mirrored
+  kOpProd = 2,    // C = A B^T, lower tiles, mirrored
+  kOpXform = 3,   // C = alpha * A B^T (full tiles) and C2 = its transpose
+  kOpUpdate = 4,  // W -= eta * alpha * A B^T (full tiles)
+  kOpIdent = 5    // C = I (lower tiles, mirrored; no contraction)
+};
+
+enum AlphaMode : int8_t { kAlphaOne = 0, kAlphaS = 1, kAlphaS2 = 2 };
+
+struct BufDesc {
+  void* ptr;
+  int64_t ld;    // leading dimension in elements
+  int32_t rows;  // valid rows
+  int32_t kpad;  // columns to contract over when used as an operand (multiple of 64)
+};
+
+struct MatDesc {
+  BufDesc buf[kNumBuf];
+  const void* grad;      // caller G (rows x cols)
+  void* mom;             // caller M (rows x cols), updated in place
+  void* copy_out;        // padded same-orientation copy of M' (rows x round_up(cols,64)) or null
+  void* trans_out;       // transposed copy of M' (cols x round_up(rows,64)) or null
+  int64_t copy_ld;
+  int64_t trans_ld;
+  int32_t rows, cols;
+  int32_t vec;           // caller rows are 16-byte aligned: vector access allowed
+  int32_t mom_prefix;    // first momentum tile of this matrix (all matrices, sorted order)
+  int32_t mom_tiles_c;   // momentum tiles along cols
+  int32_t tri_prefix;    // first lower-triangle GEMM tile (prefix over sorted order)
+  int32_t full_prefix;   // first full GEMM tile (prefix over sorted order)
+  float eta;             // lr * sqrt(max(1, rows/cols))
+};
+
+struct GroupArg {
+  int32_t first, last;   // matrix range [first, last) in the descriptor table
+  int32_t tile_begin;    // first launch tile of this group
+  int8_t kind, a, b, c, c2, e, alpha, tri;
+};
+
+struct GemmArgs {
+  const MatDesc* desc;
+  const float* scale;    // per matrix s = 1 / (||M'||_F + eps)
+  float pa, pb, pc;
+  int32_t ngroups;
+  int32_t total_tiles;
+  GroupArg g[kMaxGroups];
+};
+
+struct MomArgs {
+  const MatDesc* desc;
+  float* partials;       // one partial sum of squares per momentum tile
+  int32_t first, last;   // matrix range [first, last) of one dtype
+  int32_t tile_begin;    // mom_prefix of `first`
+  int32_t total_tiles;   // tiles of the range
+  float beta;
+};
+
+struct NormArgs {
+  const MatDesc* desc;
+  const float* partials;
+  float* scale;
+  int32_t count;
+  float eps;
+};
+
+struct AdamArgs {
+  float* p;
+  const float* g;
+  float* m;
+  float* v;
+  int64_t n;
+  float lr, beta1, beta2, eps, wd;
+  float bc1, bc2;        // 1 - beta1^t, 1 - beta2^t (computed on the host in double)
+};
+
+inline int64_t round_up(int64_t x, int64_t q) { return (x + q - 1) / q * q; }
+inline int64_t ceil_div(int64_t x, int64_t q) { return (x + q - 1) / q; }
+
+}  // namespace muon
+
+// Kernel launchers (defined in the .hip files).  Each returns a hipError_t as int.
+int muon_launch_momentum(const muon::MomArgs& a, int dtype, void* stream);
+int muon_launch_norm(const muon::NormArgs& a, void* stream);
+int muon_launch_gemm(const muon::GemmArgs& a, int dtype, void* stream);
+int muon_launch_adamw(const muon::AdamArgs& a, void* stream);

@@ -1,0 +1,74 @@
+// Host-side planning of one muon_step call: validation, shape buckets, restart sets,
+// the per-matrix op schedule in Gram space, Gram-slot assignment, workspace layout and
+// the grouped launch list.  Pure C++: no HIP call, so it runs (and is tested) without a GPU.
+#pragma once
+
+#include <string>
+#include <vector>
+
+#include "../../include/muon.h"
+#include "muon_internal.h"
+
+namespace muon {
+
+struct PlanOp {
+  int8_t kind, a, b, c, c2, e, alpha, tri;
+  int level;
+  bool same_sig(const PlanOp& o) const {
+    return kind == o.kind && a == o.a && b == o.b && c == o.c && c2 == o.c2 && e == o.e &&
+           alpha == o.alpha && tri == o.tri;
+  }
+};
+
+struct PlanMat {
+  int orig = 0;                  // index in the caller's list
+  int64_t r = 0, c = 0, m = 0, n = 0, mp = 0, np = 0;
+  bool tall = false;
+  int dtype = kBF16;
+  size_t esize = 2;
+  uint32_t restarts = 0;
+  std::vector<PlanOp> ops;
+  int64_t off[kNumBuf];          // workspace offsets of workspace-resident buffers, -1 if none
+  int64_t copy_off = -1;         // reserved padded same-orientation copy
+  int64_t trans_off = -1;        // reserved transposed copy
+  int64_t tri_tiles = 0, full_tiles = 0, mom_tiles = 0, mom_tiles_c = 0;
+  int64_t tri_prefix = 0, full_prefix = 0, mom_prefix = 0;
+  double flops = 0, bytes = 0;
+};
+
+enum LaunchKind { kLaunchMomentum = 0, kLaunchNorm = 1, kLaunchGemm = 2 };
+
+struct PlanLaunch {
+  int kind = kLaunchGemm;
+  int dtype = kBF16;
+  int level = -1;
+  int first = 0, last = 0;       // momentum: matrix range
+  std::vector<GroupArg> groups;  // gemm
+  int64_t tiles = 0;
+  double flops = 0, bytes = 0;
+};
+
+struct Plan {
+  std::vector<PlanMat> mats;     // sorted order
+  std::vector<PlanLaunch> launches;
+  int64_t desc_off = 0, scale_off = 0, partial_off = 0;
+  int64_t total_mom_tiles = 0;
+  size_t ws_bytes = 0;
+  int levels = 0;
+  double flops = 0, bytes = 0;
+};
+
+// Validate and plan.  Returns MUON_OK or a negative muon_status with *err set.
+int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, Plan* plan,
+               std::string* err);
+
+// Fill the device descriptor table for a concrete workspace base address.
+void fill_descs(const Plan& plan, const muon_matrix* mats, const muon_hparams* hp, char* ws,
+                std::vector<MatDesc>* out);
+
+// Resolve the restart set of one matrix (bit k = re-anchor before iteration k).
+uint32_t resolve_restarts(uint32_t mask, int64_t m, int64_t n, int steps);
+
+std::string describe_plan(const Plan& plan);
+
+}  // namespace muon

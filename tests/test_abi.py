@@ -1,0 +1,244 @@
+"""CPU tests of the C ABI: exported symbols, host-side validation and planning.
+
+No test here launches a kernel.  Calls that pass validation are only made when no GPU
+is visible (they then stop at the first HIP call with MUON_EHIP); pointers in these
+tests are fake host-side numbers and must never reach a device.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import re
+from pathlib import Path
+
+import pytest
+
+import newton_schulz_02_amd as nm
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "muon.h"
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_]+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n.startswith(("muon_", "adamw_"))))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"muon_step", "muon_workspace_size", "adamw_step", "muon_strerror",
+            "muon_last_error", "muon_profile_begin", "muon_profile_end"} <= set(names)
+    lib = nm.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+    assert nm.version().startswith("muon-gfx950")
+
+
+def test_strerror_covers_every_status():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert nm.strerror(code) != "unknown status"
+    assert nm.strerror(7) == "unknown status"
+
+
+HP = nm.make_hparams()
+
+
+def call_step(arr, count, hp=HP, ws=1 << 32, ws_bytes=1 << 40):
+    return nm.lib().muon_step(arr, count, ctypes.byref(hp) if hp is not None else None,
+                              ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def mats(*shapes, dtype=nm.MUON_BF16):
+    return nm.shape_array([tuple(s) for s in shapes], dtype)
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a, h: a.__setitem__(0, nm.muon_matrix(0, a[0].grad, a[0].momentum, 8, 8, 1, 0)), nm.MUON_EINVAL),
+    (lambda a, h: setattr(a[0], "rows", 0), nm.MUON_EINVAL),
+    (lambda a, h: setattr(a[0], "cols", -3), nm.MUON_EINVAL),
+    (lambda a, h: setattr(a[0], "cols", (1 << 20) + 1), nm.MUON_EINVAL),
+    (lambda a, h: setattr(a[0], "dtype", 7), nm.MUON_EINVAL),
+    (lambda a, h: setattr(a[0], "reserved", 1), nm.MUON_EINVAL),
+    (lambda a, h: setattr(a[0], "param", a[0].param + 1), nm.MUON_EINVAL),
+    (lambda a, h: setattr(h, "lr", float("nan")), nm.MUON_EINVAL),
+    (lambda a, h: setattr(h, "beta", float("inf")), nm.MUON_EINVAL),
+    (lambda a, h: setattr(h, "eps", -1.0), nm.MUON_EINVAL),
+    (lambda a, h: setattr(h, "ns_steps", 32), nm.MUON_EINVAL),
+    (lambda a, h: setattr(h, "ns_steps", -1), nm.MUON_EINVAL),
+    (lambda a, h: setattr(a[0], "grad", a[0].param), nm.MUON_EALIAS),
+    (lambda a, h: setattr(a[0], "momentum", a[0].param), nm.MUON_EALIAS),
+    (lambda a, h: setattr(a[1], "param", a[0].momentum + 64), nm.MUON_EALIAS),
+    (lambda a, h: setattr(a[1], "grad", a[0].param + 64), nm.MUON_EALIAS),
+])
+def test_validation_rejects_before_any_hip_call(mutate, code):
+    arr = mats((8, 8), (8, 8))
+    hp = nm.make_hparams()
+    mutate(arr, hp)
+    for fn in ("step", "size"):
+        if fn == "step":
+            rc = call_step(arr, 2, hp)
+        else:
+            out = ctypes.c_size_t(0)
+            rc = nm.lib().muon_workspace_size(arr, 2, ctypes.byref(hp), ctypes.byref(out))
+        assert rc == code, (fn, rc, nm.last_error())
+        assert nm.last_error()
+
+
+def test_gradients_may_overlap_each_other():
+    arr = mats((8, 8), (8, 8))
+    arr[1].grad = arr[0].grad  # shared read-only gradient: allowed
+    out = ctypes.c_size_t(0)
+    assert nm.lib().muon_workspace_size(arr, 2, ctypes.byref(HP), ctypes.byref(out)) == nm.MUON_OK
+
+
+def test_null_arguments():
+    out = ctypes.c_size_t(0)
+    assert nm.lib().muon_workspace_size(None, 1, ctypes.byref(HP), ctypes.byref(out)) == nm.MUON_EINVAL
+    assert nm.lib().muon_workspace_size(mats((4, 4)), 1, None, ctypes.byref(out)) == nm.MUON_EINVAL
+    assert nm.lib().muon_workspace_size(mats((4, 4)), 1, ctypes.byref(HP), None) == nm.MUON_EINVAL
+    assert nm.lib().muon_workspace_size(mats((4, 4)), -1, ctypes.byref(HP), ctypes.byref(out)) == nm.MUON_EINVAL
+    assert call_step(mats((4, 4)), 1, ws=0) == nm.MUON_EINVAL
+    assert call_step(mats((4, 4)), 1, ws=(1 << 32) + 64) == nm.MUON_EINVAL  # not 256-aligned
+
+
+def test_workspace_too_small_is_enospc():
+    arr = mats((100, 300))
+    need = nm.workspace_size_raw(arr, 1, HP)
+    assert call_step(arr, 1, ws_bytes=need - 1) == nm.MUON_ENOSPC
+    assert "needs" in nm.last_error()
+
+
+def test_count_zero_is_a_no_op():
+    assert call_step(mats((4, 4)), 0) == nm.MUON_OK
+    assert nm.workspace_size_raw(mats((4, 4)), 0, HP) == 0
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="valid call with fake pointers: only without a GPU")
+def test_valid_call_without_gpu_reports_hip_error():
+    assert call_step(mats((64, 64)), 1) == nm.MUON_EHIP
+    assert "hipGetDevice" in nm.last_error()
+    hp = nm.adamw_hparams(1e-3, 0.9, 0.95, 1e-8, 0.1, 1)
+    rc = nm.lib().adamw_step(ctypes.c_void_p(1 << 20), ctypes.c_void_p(2 << 20), ctypes.c_void_p(3 << 20),
+                             ctypes.c_void_p(4 << 20), 16, ctypes.byref(hp), None)
+    assert rc == nm.MUON_EHIP
+
+
+def test_adamw_validation():
+    lib = nm.lib()
+    P = [ctypes.c_void_p(k << 20) for k in (1, 2, 3, 4)]
+
+    def run(n=16, **kw):
+        h = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
+        h.update(kw)
+        hp = nm.adamw_hparams(h["lr"], h["beta1"], h["beta2"], h["eps"], h["weight_decay"], h["step"])
+        return lib.adamw_step(*P, n, ctypes.byref(hp), None)
+
+    assert run(step=0) == nm.MUON_EINVAL
+    assert run(beta1=1.0) == nm.MUON_EINVAL
+    assert run(lr=float("nan")) == nm.MUON_EINVAL
+    assert run(n=-1) == nm.MUON_EINVAL
+    assert run(n=0) == nm.MUON_OK
+    hp = nm.adamw_hparams(1e-3, 0.9, 0.95, 1e-8, 0.1, 1)
+    assert lib.adamw_step(P[0], P[0], P[2], P[3], 16, ctypes.byref(hp), None) == nm.MUON_EALIAS
+    assert lib.adamw_step(ctypes.c_void_p(2), P[1], P[2], P[3], 16, ctypes.byref(hp), None) == nm.MUON_EINVAL
+
+
+# --- planning ------------------------------------------------------------------------------
+
+def plan(shapes, dtype=nm.MUON_BF16, **hp):
+    arr = mats(*shapes, dtype=dtype)
+    return nm.plan_describe(arr, len(shapes), nm.make_hparams(**hp))
+
+
+@pytest.mark.parametrize("shape,steps,want", [
+    ((4096, 4096), 5, {2, 3, 4}),
+    ((1024, 1024), 5, {2, 3, 4}),
+    ((4096, 11008), 5, set()),
+    ((11008, 4096), 5, set()),
+    ((1024, 1535), 5, {2, 3, 4}),
+    ((1535, 1024), 5, {2, 3, 4}),
+    ((1024, 1536), 5, set()),
+    ((512, 512), 7, {2, 3, 4, 5, 6}),
+    ((512, 512), 3, {2}),
+    ((512, 512), 2, set()),
+    ((512, 512), 0, set()),
+])
+def test_auto_restart_sets(shape, steps, want):
+    p = plan([shape], steps=steps)
+    mask = p["matrices"][0]["restarts"]
+    assert {k for k in range(32) if mask >> k & 1} == want
+
+
+def test_explicit_restart_mask_clips_bit0_and_range():
+    p = plan([(64, 64)], restart_mask=0b1111111, steps=5)
+    assert p["matrices"][0]["restarts"] == 0b11110
+
+
+def _flops_rect(m, n, k=5):
+    # symmetric m x m x k products count m(m+1)k; full products 2 m n k.
+    return m * (m + 1) * n + (4 * k - 3) * m * (m + 1) * m + 2 * m * m * n
+
+
+def test_flop_count_matches_the_counting_rule():
+    p = plan([(4096, 11008)])
+    assert p["flops"] == _flops_rect(4096, 11008)
+    # Square with restarts {2, 3, 4}: 4 SYRKs, 8 Gram products, 3 re-anchors and the apply.
+    m = 4096
+    want = 4 * m * (m + 1) * m + 8 * m * (m + 1) * m + 4 * 2 * m ** 3
+    assert plan([(m, m)])["flops"] == want
+
+
+def test_layer_flops_and_launch_count():
+    from newton_schulz_02_amd.workloads import WORKLOADS
+
+    wl = WORKLOADS["layer4096_bf16"]
+    p = plan([(s.rows, s.cols) for s in wl.matrices])
+    assert math.isclose(p["flops"], 1.0666e13, rel_tol=1e-3)
+    kinds = [L["kind"] for L in p["launches"]]
+    assert kinds.count("momentum") == 1 and kinds.count("norm") == 1
+    assert kinds.count("gemm") == p["levels"] <= 17
+
+
+def test_buckets_are_contiguous_and_sorted():
+    shapes = [(256, 256), (512, 2048), (256, 256), (2048, 512), (512, 2048), (256, 256)]
+    p = plan(shapes)
+    order = [(m["restarts"], m["tall"], m["m"], m["n"]) for m in p["matrices"]]
+    assert order == sorted(order)
+    assert sorted(m["orig"] for m in p["matrices"]) == list(range(len(shapes)))
+    for L in p["launches"]:
+        for g in L["groups"]:
+            assert 0 <= g["first"] < g["last"] <= len(shapes)
+
+
+def test_mixed_dtypes_get_separate_launches():
+    arr = nm.shape_array([(64, 128, nm.MUON_BF16), (64, 128, nm.MUON_F32)])
+    p = nm.plan_describe(arr, 2, HP)
+    moms = [L for L in p["launches"] if L["kind"] == "momentum"]
+    assert sorted(L["dtype"] for L in moms) == [1, 2]
+    for L in p["launches"]:
+        if L["kind"] == "gemm":
+            dt = {p["matrices"][i]["dtype"] for g in L["groups"] for i in range(g["first"], g["last"])}
+            assert dt == {L["dtype"]}
+
+
+def test_workspace_size_independent_of_pointers_and_grows_with_count():
+    a1 = nm.shape_array([(300, 700)])
+    a2 = nm.shape_array([(300, 700)])
+    a2[0].param += 1 << 36
+    a2[0].grad += 1 << 36
+    a2[0].momentum += 1 << 36
+    s1 = nm.workspace_size_raw(a1, 1, HP)
+    assert s1 == nm.workspace_size_raw(a2, 1, HP)
+    assert nm.workspace_size_raw(nm.shape_array([(300, 700)] * 2), 2, HP) > s1
+    assert s1 % 256 == 0
