@@ -141,6 +141,14 @@ typedef struct muon_kernel_stat {
 int muon_profile_begin(void);
 int muon_profile_end(muon_kernel_stat* out, int32_t max, int32_t* count);
 
+/* Test hooks (host only): the tile orders used by the MFMA kernel.
+ * muon_debug_tile_order: tile t of one matrix -> (ti[t], tj[t]); tri != 0 walks the lower
+ * triangle of a tm x tm tile grid, else the full tm x tn grid.  Returns the tile count;
+ * ti and tj must hold that many ints.
+ * muon_debug_xcd_remap: workgroup w -> logical tile out[w] for a grid of `total`. */
+int muon_debug_tile_order(int tri, int tm, int tn, int* ti, int* tj);
+int muon_debug_xcd_remap(int total, int* out);
+
 const char* muon_strerror(int status); /* static string */
 const char* muon_last_error(void);     /* detail of the last failure on this thread */
 const char* muon_version(void);

@@ -79,6 +79,8 @@ _SIGNATURES = {
     "muon_last_error": (c_char_p, []),
     "muon_version": (c_char_p, []),
     "muon_shutdown": (None, []),
+    "muon_debug_tile_order": (c_int, [c_int, c_int, c_int, POINTER(c_int), POINTER(c_int)]),
+    "muon_debug_xcd_remap": (c_int, [c_int, POINTER(c_int)]),
 }
 
 _lib = None
@@ -257,6 +259,21 @@ def adamw_step(p, g, m, v, *, lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_d
     _check(lib().adamw_step(c_void_p(p.data_ptr()), c_void_p(g.data_ptr()), c_void_p(m.data_ptr()),
                             c_void_p(v.data_ptr()), p.numel(), ctypes.byref(hp),
                             _stream_handle(stream, p.device)))
+
+
+def tile_order(tri: bool, tm: int, tn: int = 0):
+    """Test hook: the (ti, tj) order in which the MFMA kernel walks one matrix's tiles."""
+    n = tm * (tm + 1) // 2 if tri else tm * tn
+    ti, tj = (c_int * max(n, 1))(), (c_int * max(n, 1))()
+    lib().muon_debug_tile_order(int(bool(tri)), tm, tn, ti, tj)
+    return list(zip(ti[:n], tj[:n]))
+
+
+def xcd_remap(total: int):
+    """Test hook: logical tile of each workgroup id in a grid of `total`."""
+    out = (c_int * max(total, 1))()
+    lib().muon_debug_xcd_remap(total, out)
+    return list(out[:total])
 
 
 def profile_begin() -> None:

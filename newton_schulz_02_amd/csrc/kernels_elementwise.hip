@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256) void k_momentum(MomArgs a) {
 __global__ __launch_bounds__(256) void k_norm(NormArgs a) {
   __shared__ double red[256];
   const MatDesc& d = a.desc[blockIdx.x];
-  const int ntiles = ((d.rows + kEwTile - 1) / kEwTile) * d.mom_tiles_c;
+  const int ntiles = d.mom_tiles_r * d.mom_tiles_c;
   double acc = 0.0;
   for (int t = threadIdx.x; t < ntiles; t += 256) acc += double(a.partials[d.mom_prefix + t]);
   red[threadIdx.x] = acc;

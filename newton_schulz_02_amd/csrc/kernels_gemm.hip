@@ -11,38 +11,84 @@
 // lower-triangle tiles only; each computed element (i >= j) is stored at (i, j) and at
 // (j, i), so every stored iterate is exactly symmetric.
 //
-// Tile: 256 x 256 x 64 (bf16) or 256 x 256 x 32 (fp32) per LDS stage, 8 waves of 64 lanes
-// in a 2 x 4 grid, each wave owning 128 x 64 = 4 x 2 blocks of 32 x 32 MFMA accumulators
-// (v_mfma_f32_32x32x16_bf16 or v_mfma_f32_32x32x2_f32, fp32 accumulate).  Operand rows
-// are 128 bytes per stage; LDS rows are padded to 144 bytes so the 16-byte fragment reads
-// of 8 consecutive rows hit distinct bank groups.  Two LDS stages with a register
-// prefetch of the next stage overlap global loads with the MFMA work.
+// Main loop: 8 waves of 64 lanes in a 2 x 4 grid, each wave owning 128 x 64 = 4 x 2 blocks
+// of 32 x 32 MFMA accumulators (v_mfma_f32_32x32x16_bf16, or v_mfma_f32_32x32x2_f32 for
+// fp32; fp32 accumulate).  A stage holds kRowBytes of every operand row (64 bf16 or 32
+// fp32 with 128-byte rows).  Operands go straight from global memory to LDS
+// (global_load_lds_dwordx4: 16 bytes per lane, 1 KB per wave instruction), so no VGPRs
+// or LDS-write instructions are spent on staging.  LDS rows are unpadded; the 16-byte
+// chunk c of row r sits at chunk position c ^ swz(r).  The LDS serves 16 lanes of a
+// 16-byte read per cycle from 64 four-byte banks (256 bytes), and a fragment read has 16
+// consecutive lanes on 16 consecutive rows at the same chunk: with 128-byte rows, two
+// rows share a 256-byte bank window, so swz(r) = (r / 2) mod 8 puts the 16 rows on 16
+// distinct 16-byte bank groups (64-byte rows: four per window, swz(r) = (r / 4) mod 4).  kStages stages form a ring;
+// loads run kStages-1 stages ahead of the MFMAs, with one barrier per stage.  Each stage
+// is its own __shared__ array and the k loop is unrolled by kStages, so every LDS access
+// names its array statically: the compiler can then tell that the loads in flight target
+// other stages and does not make the fragment reads wait for them.
+//
+// Operand rows past the end of an operand are clamped to its last row: they only feed
+// output rows or columns that are never stored, and every load stays in bounds.
 //
 // Epilogue: the accumulators are staged through LDS as fp32, one 128-row half of the tile
 // at a time, so that the epilogue math reads each input once and both the direct store
 // (rows of C) and the mirrored/transposed store (rows of C^T) are coalesced.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "muon_internal.h"
+#include "tile_order.h"
 
 using namespace muon;
+
+#ifndef MUON_GEMM_STAGES
+#define MUON_GEMM_STAGES 2
+#endif
+#ifndef MUON_GEMM_ROW_BYTES
+#define MUON_GEMM_ROW_BYTES 128
+#endif
 
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kThreads = 512;
-constexpr int kWavesN = 4;                 // waves along the tile columns
-constexpr int kFragN = kTile / kWavesN / 32;  // 32-wide blocks per wave along N (2)
-constexpr int kEpLd = kTile + 4;           // fp32 leading dimension of the staged half tile
-constexpr int kRowBytes = 128;             // bytes of one operand row per LDS stage
-constexpr int kLdsRow = kRowBytes + 16;    // padded LDS row
-constexpr int kOperandBytes = kTile * kLdsRow;
+constexpr int kWaves = kThreads / 64;
+constexpr int kWavesN = 4;                     // waves along the tile columns
+constexpr int kFragN = kTile / kWavesN / 32;   // 32-wide blocks per wave along N (2)
+constexpr int kStages = MUON_GEMM_STAGES;
+constexpr int kEpLd = kTile / kStages + 1;     // fp32 leading dimension of a staged block
+                                               // (odd: strided reads spread over the banks)
+constexpr int kRowBytes = MUON_GEMM_ROW_BYTES; // bytes of one operand row per stage
+constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks per row
+constexpr int kOperandBytes = kTile * kRowBytes;
 constexpr int kStageBytes = 2 * kOperandBytes;
-constexpr int kChunksPerThread = kTile * kRowBytes / 16 / kThreads;  // 4
-constexpr int kChunkRows = kThreads / (kRowBytes / 16);               // 64 rows per chunk slab
-static_assert(128 * kEpLd * 4 <= 2 * kStageBytes, "staged half tile must fit in LDS");
+constexpr int kRowsPerInst = 1024 / kRowBytes; // rows one wave instruction fills
+constexpr int kInstPerOperand = kOperandBytes / 1024 / kWaves;  // per wave per stage
+// The epilogue stages a 128-row half tile in fp32, split by column block across the stage
+// arrays: array q holds columns [q kEpW, (q + 1) kEpW) with leading dimension kEpLd.
+constexpr int kEpW = kTile / kStages;
+constexpr int kEpArrBytes = 128 * kEpLd * 4;
+// bf16 outputs of the Gram products and re-anchors are staged once, transposed: T-row c
+// (a tile column) holds the 256 tile rows; T-rows 0..127 in lds0, 128..255 in lds1.
+constexpr int kTs = kTile + 8;                 // bf16 T-row stride (528 bytes: 16-byte aligned)
+constexpr int kTArrBytes = 128 * kTs * 2;
+constexpr int kMaxAB = kStageBytes > kEpArrBytes ? kStageBytes : kEpArrBytes;
+constexpr int kArrBytes = kMaxAB > kTArrBytes ? kMaxAB : kTArrBytes;
+static_assert(kRowBytes == 128 || kRowBytes == 64, "row bytes per stage");
+static_assert(kStages == 2 || kStages == 4, "stage count (the epilogue splits 256 columns)");
+static_assert(kStages * kArrBytes <= 160 * 1024, "LDS budget");
+static_assert(kInstPerOperand >= 1, "every wave loads part of each operand");
+static_assert(kKPad % (kStages * kRowBytes / 4) == 0 && kKPad % (kStages * kRowBytes / 2) == 0,
+              "padded contraction dims must hold whole blocks of stages");
+
+// Chunk position of 16-byte chunk c in LDS row r is c ^ swz(r) (a bijection on a row).
+__device__ __forceinline__ int swz(int r) {
+  return kRowBytes == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
 
 __device__ __forceinline__ float to_f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 __device__ __forceinline__ float to_f(float f) { return f; }
@@ -51,22 +97,13 @@ __device__ __forceinline__ uint16_t from_f(float f, uint16_t*) {
 }
 __device__ __forceinline__ float from_f(float f, float*) { return f; }
 
-// Lower-triangle tile index t -> (ti, tj), ti >= tj, row-major over the triangle.
-__device__ __forceinline__ void tri_decode(int t, int& ti, int& tj) {
-  int i = int((sqrtf(8.0f * float(t) + 1.0f) - 1.0f) * 0.5f);
-  while ((i + 1) * (i + 2) / 2 <= t) ++i;
-  while (i * (i + 1) / 2 > t) --i;
-  ti = i;
-  tj = t - i * (i + 1) / 2;
-}
-
 // MFMA step over one 16-byte fragment per operand.
 template <typename S>
 struct Mma;
 
 template <>
 struct Mma<uint16_t> {
-  static constexpr int kStageK = 64;   // k elements per stage
+  static constexpr int kStageK = kRowBytes / 2;   // k elements per stage
   __device__ __forceinline__ static void step(const uint4& a, const uint4& b, f32x16& acc) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
@@ -75,7 +112,7 @@ struct Mma<uint16_t> {
 
 template <>
 struct Mma<float> {
-  static constexpr int kStageK = 32;
+  static constexpr int kStageK = kRowBytes / 4;
   // The fragment holds 4 consecutive k values per lane; MFMA e contracts over element e
   // of both operands (A and B use the same k map, so the sum covers all 8 k values).
   __device__ __forceinline__ static void step(const uint4& a, const uint4& b, f32x16& acc) {
@@ -85,6 +122,59 @@ struct Mma<float> {
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
   }
 };
+
+// Wait until at most n vector-memory operations of this wave are outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14].
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// Workgroup barrier for the main loop.  __syncthreads() carries a release fence that
+// would wait for every load in flight (LDS-DMA loads count as LDS writes), draining the
+// pipeline; here each wave has already waited for the loads of the stage it is about to
+// read (wait_vm), and its LDS reads of the previous stage completed before the MFMAs that
+// consumed them.  The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Calls f(integral_constant<int, S>) for S = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Eight consecutive elements of S as one 16- or 32-byte vector.
+template <typename S>
+struct Vec8 {
+  S v[8];
+};
+template <typename S>
+__device__ __forceinline__ void load8(const S* p, Vec8<S>& x) {
+  if constexpr (sizeof(S) == 2) {
+    *reinterpret_cast<uint4*>(x.v) = *reinterpret_cast<const uint4*>(p);
+  } else {
+    reinterpret_cast<uint4*>(x.v)[0] = reinterpret_cast<const uint4*>(p)[0];
+    reinterpret_cast<uint4*>(x.v)[1] = reinterpret_cast<const uint4*>(p)[1];
+  }
+}
+template <typename S>
+__device__ __forceinline__ void store8(S* p, const Vec8<S>& x) {
+  if constexpr (sizeof(S) == 2) {
+    *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(x.v);
+  } else {
+    reinterpret_cast<uint4*>(p)[0] = reinterpret_cast<const uint4*>(x.v)[0];
+    reinterpret_cast<uint4*>(p)[1] = reinterpret_cast<const uint4*>(x.v)[1];
+  }
+}
 
 // Value of the symmetric-output epilogues at (gi, gj); x is the accumulated product.  E is
 // read at (er, ec), which is (gi, gj) or its mirror: stored iterates are exactly symmetric.
@@ -101,10 +191,21 @@ __device__ __forceinline__ float tri_value(int kind, int gi, int gj, int m, floa
 
 template <typename S>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds0[kArrBytes];
+  __shared__ __attribute__((aligned(1024))) char lds1[kArrBytes];
+  __shared__ __attribute__((aligned(1024))) char lds2[kStages > 2 ? kArrBytes : 16];
+  __shared__ __attribute__((aligned(1024))) char lds3[kStages > 3 ? kArrBytes : 16];
+  // Stage array s, named statically when s is a compile-time constant.
+  auto stage_of = [&](auto sc) -> char* {
+    constexpr int s = decltype(sc)::value % kStages;
+    if constexpr (s == 0) return lds0;
+    else if constexpr (s == 1) return lds1;
+    else if constexpr (s == 2) return lds2;
+    else return lds3;
+  };
 
   // ---- which group, matrix and tile --------------------------------------------------
-  const int bid = int(blockIdx.x);
+  const int bid = xcd_remap(int(blockIdx.x), int(gridDim.x));
   GroupArg g = args.g[0];
 #pragma unroll
   for (int q = 1; q < kMaxGroups; ++q)
@@ -129,11 +230,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
   const int cols_out = B.rows;
   int ti, tj;
   if (g.tri) {
-    tri_decode(t, ti, tj);
+    tri_band_decode(t, (rows_out + kTile - 1) / kTile, ti, tj);
   } else {
-    const int tn = (cols_out + kTile - 1) / kTile;
-    ti = t / tn;
-    tj = t % tn;
+    full_band_decode(t, (rows_out + kTile - 1) / kTile, (cols_out + kTile - 1) / kTile, ti, tj);
   }
   const int row0 = ti * kTile;
   const int col0 = tj * kTile;
@@ -147,7 +246,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
   const int lk = lane >> 5;
   // In a diagonal tile the waves with rows [0,128) and columns [128,256) lie strictly above
   // the diagonal: nothing they compute is stored.
-  const bool idle = (g.tri && ti == tj && wm == 0 && wn >= 2) || ident;
+  const bool above = g.tri && ti == tj && wm == 0 && wn >= 2;
+  const bool idle = above || ident;
 
   f32x16 acc[4][kFragN];
 #pragma unroll
@@ -157,86 +257,201 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // ---- main loop -----------------------------------------------------------------------
+  // ---- loads: wave `wave` fills rows [wave*R, wave*R + R) of each operand per stage,
+  // R = kInstPerOperand * kRowsPerInst, one instruction per kRowsPerInst rows.  Lane l of
+  // an instruction writes LDS bytes [16 l, 16 l + 16) of its 1 KB block: row l / kChunks
+  // of the block, chunk position l % kChunks, holding global chunk (position ^ swz(row)).
   const int ksteps = ident ? 0 : A.kpad / Mma<S>::kStageK;
-  const char* Ab = static_cast<const char*>(A.ptr);
-  const char* Bb = static_cast<const char*>(B.ptr);
   const int64_t lda = A.ld * int64_t(sizeof(S));
   const int64_t ldb = B.ld * int64_t(sizeof(S));
-  const int crow = tid >> 3;         // chunk row within a 64-row slab
-  const int cbyte = (tid & 7) * 16;  // chunk byte within the row
-  // Chunk q of this thread is row (crow + 64q) of the tile; rows past the operand read 0.
-  const int a_lim = A.rows - row0 - crow;
-  const int b_lim = B.rows - col0 - crow;
-  const char* a_base = Ab + int64_t(row0 + crow) * lda + cbyte;
-  const char* b_base = Bb + int64_t(col0 + crow) * ldb + cbyte;
-  const int64_t a_step = kChunkRows * lda;
-  const int64_t b_step = kChunkRows * ldb;
-  uint4 ra[kChunksPerThread], rb[kChunksPerThread];
-  auto gload = [&](int ks) {
+  const int lrow = lane / kChunks;
+  const int lpos = lane % kChunks;
+  const char* a_src[kInstPerOperand];
+  const char* b_src[kInstPerOperand];
+#pragma unroll
+  for (int j = 0; j < kInstPerOperand; ++j) {
+    const int r = (wave * kInstPerOperand + j) * kRowsPerInst + lrow;  // tile row
+    const int chunk = lpos ^ swz(r);
+    const int ra = min(row0 + r, A.rows - 1);
+    const int rb = min(col0 + r, B.rows - 1);
+    a_src[j] = static_cast<const char*>(A.ptr) + int64_t(ra) * lda + chunk * 16;
+    b_src[j] = static_cast<const char*>(B.ptr) + int64_t(rb) * ldb + chunk * 16;
+  }
+  // Issue the loads of k-step ks into stage array st.
+  auto issue = [&](int ks, char* st) {
     const int64_t koff = int64_t(ks) * kRowBytes;
 #pragma unroll
-    for (int q = 0; q < kChunksPerThread; ++q) {
-      ra[q] = kChunkRows * q < a_lim ? *reinterpret_cast<const uint4*>(a_base + q * a_step + koff)
-                                     : make_uint4(0, 0, 0, 0);
-      rb[q] = kChunkRows * q < b_lim ? *reinterpret_cast<const uint4*>(b_base + q * b_step + koff)
-                                     : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < kInstPerOperand; ++j) {
+      const int blk = (wave * kInstPerOperand + j) * 1024;
+      __builtin_amdgcn_global_load_lds(a_src[j] + koff, (lds_void*)(st + blk), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(b_src[j] + koff, (lds_void*)(st + kOperandBytes + blk), 16, 0, 0);
     }
   };
-  auto lstore = [&](int stage) {
-    char* As = smem + stage * kStageBytes;
-    char* Bs = As + kOperandBytes;
-#pragma unroll
-    for (int q = 0; q < kChunksPerThread; ++q) {
-      const int rr = crow + kChunkRows * q;
-      *reinterpret_cast<uint4*>(As + rr * kLdsRow + cbyte) = ra[q];
-      *reinterpret_cast<uint4*>(Bs + rr * kLdsRow + cbyte) = rb[q];
-    }
-  };
+  constexpr int kLoadsPerStage = 2 * kInstPerOperand;
 
-  if (ksteps > 0) {
-    gload(0);
-    lstore(0);
-    __syncthreads();
-  }
-  for (int ks = 0; ks < ksteps; ++ks) {
-    const int stage = ks & 1;
-    if (ks + 1 < ksteps) gload(ks + 1);
+  // Prologue: stages 0 .. kStages-2 in flight.
+  static_for<0, kStages - 1>([&](auto sc) {
+    if (sc.value < ksteps) issue(sc.value, stage_of(sc));
+  });
+
+  // Fragment rows of this lane (+ 32 i for A, + 32 j for B).
+  const int a_row = wm * 128 + lr;
+  const int b_row = wn * 64 + lr;
+  // One k-step: wait until this wave's loads of stage ks landed (at most `pending` newer
+  // loads remain), barrier, issue the loads kStages-1 steps ahead, run the MFMAs.
+  auto kstep = [&](int ks, auto sc, auto pending) {
+    wait_vm<decltype(pending)::value>();
+    stage_barrier();  // all waves' loads of stage ks landed; stage ks-1 is free again
+    if (ks + kStages - 1 < ksteps)
+      issue(ks + kStages - 1, stage_of(std::integral_constant<int, decltype(sc)::value + kStages - 1>{}));
     if (!idle) {
-      const char* As = smem + stage * kStageBytes + (wm * 128 + lr) * kLdsRow + lk * 16;
-      const char* Bs = smem + stage * kStageBytes + kOperandBytes + (wn * 64 + lr) * kLdsRow + lk * 16;
+      const char* st = stage_of(sc);
 #pragma unroll
       for (int kk = 0; kk < kRowBytes / 32; ++kk) {
+        const int c = 2 * kk + lk;   // 16-byte chunk of this lane's 8 (or 4) k values
         uint4 fa[4], fb[kFragN];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          fa[i] = *reinterpret_cast<const uint4*>(As + i * 32 * kLdsRow + kk * 32);
+        for (int i = 0; i < 4; ++i) {
+          const int r = a_row + 32 * i;
+          fa[i] = *reinterpret_cast<const uint4*>(st + r * kRowBytes + ((c ^ swz(r)) << 4));
+        }
 #pragma unroll
-        for (int j = 0; j < kFragN; ++j)
-          fb[j] = *reinterpret_cast<const uint4*>(Bs + j * 32 * kLdsRow + kk * 32);
+        for (int j = 0; j < kFragN; ++j) {
+          const int r = b_row + 32 * j;
+          fb[j] = *reinterpret_cast<const uint4*>(st + kOperandBytes + r * kRowBytes +
+                                                  ((c ^ swz(r)) << 4));
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < kFragN; ++j) Mma<S>::step(fa[i], fb[j], acc[i][j]);
       }
     }
-    if (ks + 1 < ksteps) lstore(stage ^ 1);
-    __syncthreads();
+  };
+  // ksteps is a multiple of kStages (contraction dims are padded to kKPad).  Full blocks
+  // keep kStages-2 stages in flight behind the one being read; the last block drains.
+  int kb = 0;
+  for (; kb + kStages < ksteps; kb += kStages) {
+    static_for<0, kStages>([&](auto sc) {
+      kstep(kb + sc.value, sc, std::integral_constant<int, (kStages - 2) * kLoadsPerStage>{});
+    });
   }
+  if (kb < ksteps) {
+    static_for<0, kStages>([&](auto sc) {
+      constexpr int left = kStages - 1 - decltype(sc)::value;   // stages after this one
+      constexpr int ahead = left < kStages - 2 ? left : kStages - 2;
+      kstep(kb + sc.value, sc, std::integral_constant<int, ahead * kLoadsPerStage>{});
+    });
+  }
+  __syncthreads();  // the epilogue reuses the LDS
 
   // ---- epilogue ------------------------------------------------------------------------
   // acc[i][j][r] holds tile element (128 wm + 32 i + 8 (r/4) + 4 lk + r%4, 64 wn + 32 j + lr).
   float alpha = 1.0f;
   if (g.alpha == kAlphaS) alpha = args.scale[lo];
   else if (g.alpha == kAlphaS2) alpha = args.scale[lo] * args.scale[lo];
-  float* ep = reinterpret_cast<float*>(smem);
   S* Cp = static_cast<S*>(C.ptr);
   const int64_t ldc = C.ld;
   const S* E = g.e >= 0 ? static_cast<const S*>(d.buf[g.e].ptr) : nullptr;
   const int64_t lde = g.e >= 0 ? d.buf[g.e].ld : 0;
   const float pa = args.pa, pb = args.pb, pc = args.pc;
-  const int m = rows_out;   // symmetric outputs: valid rows/cols
+  const int m = rows_out;    // symmetric outputs: valid rows/cols
   const int cstore = C.kpad; // symmetric outputs: stored columns (zero beyond m)
+
+  // bf16 Gram products and re-anchors: each value is formed once, in registers, from its
+  // accumulator (and, for the polynomial, the iterate read transposed: it is symmetric),
+  // rounded to bf16 and staged transposed in LDS; then two copy passes store the rows of
+  // C (direct) and of C^T (mirror or transposed output) with 16-byte stores.
+  if constexpr (sizeof(S) == 2) {
+    if (kind != kOpUpdate) {
+      auto t_row = [&](int c) -> uint16_t* {
+        return reinterpret_cast<uint16_t*>(c < 128 ? lds0 : lds1) + (c & 127) * kTs;
+      };
+      const bool xform = kind == kOpXform;
+      if (!above) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < kFragN; ++j)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const int lrow = 128 * wm + 32 * i + 8 * r4 + 4 * lk;  // 4 rows lrow .. lrow+3
+              const int lcol = 64 * wn + 32 * j + lr;
+              const int gi0 = row0 + lrow, gj = col0 + lcol;
+              uint2 e4 = make_uint2(0, 0);
+              if (kind == kOpPoly && gj < m && gi0 < m)
+                e4 = *reinterpret_cast<const uint2*>(E + int64_t(gj) * lde + gi0);
+              const uint16_t* ev = reinterpret_cast<const uint16_t*>(&e4);
+              uint16_t o[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int gi = gi0 + q;
+                const float x = acc[i][j][4 * r4 + q];
+                float val = 0.0f;
+                if (xform) {
+                  if (gi < rows_out && gj < cols_out) val = alpha * x;
+                } else if (gi < m && gj < m) {
+                  if (kind == kOpSyrk) val = alpha * x;
+                  else if (kind == kOpPoly) val = (gi == gj ? pa : 0.0f) + pb * to_f(ev[q]) + pc * x;
+                  else if (kind == kOpIdent) val = gi == gj ? 1.0f : 0.0f;
+                  else val = x;
+                }
+                o[q] = from_f(val, static_cast<uint16_t*>(nullptr));
+              }
+              *reinterpret_cast<uint2*>(t_row(lcol) + lrow) = *reinterpret_cast<const uint2*>(o);
+            }
+      }
+      __syncthreads();
+      // Transposed-side pass: row gj = col0 + c of the output gets tile rows r .. r+7.
+      S* Tp = xform ? static_cast<S*>(d.buf[g.c2].ptr) : Cp;
+      const int64_t ldt = xform ? d.buf[g.c2].ld : ldc;
+      const int t_rows = xform ? d.buf[g.c2].rows : m;          // valid output rows
+      const int t_cols = xform ? d.buf[g.c2].kpad : cstore;     // stored output columns
+      for (int idx = tid; idx < kTile * 32; idx += kThreads) {
+        const int c = idx / 32, r = (idx % 32) * 8;
+        const int gj = col0 + c, gi = row0 + r;
+        if (gj >= t_rows || gi >= t_cols) continue;
+        if (!xform && gi + 7 <= gj) continue;  // chunk on or above the diagonal
+        Vec8<S> v;
+        *reinterpret_cast<uint4*>(v.v) = *reinterpret_cast<const uint4*>(t_row(c) + r);
+        if (xform || (gi > gj && gi + 7 < t_cols)) {
+          store8(Tp + int64_t(gj) * ldt + gi, v);
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (gi + e > gj && gi + e < t_cols) Tp[int64_t(gj) * ldt + gi + e] = v.v[e];
+        }
+      }
+      // Direct pass: row gi = row0 + r of C gets tile columns c .. c+7.  Lanes cover 8 rows
+      // by 8 column chunks, so each store instruction writes 8 rows x 128 bytes.
+      const int d_rows = xform ? C.rows : m;
+      const int d_cols = xform ? C.kpad : cstore;
+      for (int idx = tid; idx < kTile * 32; idx += kThreads) {
+        // 64-lane block b: rows 8 (b % 32) .. +7, chunks 8 (b / 32) .. +7 (columns 64 (b / 32) ..).
+        const int b = idx / 64, l = idx % 64;
+        const int r = 8 * (b % 32) + (l & 7), c = 64 * (b / 32) + 8 * (l >> 3);
+        const int gi = row0 + r, gj = col0 + c;
+        if (gi >= d_rows || gj >= d_cols) continue;
+        if (!xform && gi < gj) continue;      // chunk above the diagonal
+        Vec8<S> v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v.v[e] = t_row(c + e)[r];
+        if (xform || (gi >= gj + 7 && gj + 7 < d_cols)) {
+          store8(Cp + int64_t(gi) * ldc + gj, v);
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (gi >= gj + e && gj + e < d_cols) Cp[int64_t(gi) * ldc + gj + e] = v.v[e];
+        }
+      }
+      return;
+    }
+  }
+
+  // Staged fp32 value at (row rr of the half, tile column cc).
+  auto ep_at = [&](int rr, int cc) -> float& {
+    const int q = cc / kEpW;
+    char* base = q == 0 ? lds0 : q == 1 ? lds1 : q == 2 ? lds2 : lds3;
+    return reinterpret_cast<float*>(base)[rr * kEpLd + cc % kEpW];
+  };
 
   for (int half = 0; half < 2; ++half) {
     const int hr0 = row0 + half * 128;  // first row of this half
@@ -248,87 +463,119 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
           for (int j = 0; j < kFragN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              ep[(32 * i + 8 * (r >> 2) + 4 * lk + (r & 3)) * kEpLd + 64 * wn + 32 * j + lr] =
-                  acc[i][j][r];
+              ep_at(32 * i + 8 * (r >> 2) + 4 * lk + (r & 3), 64 * wn + 32 * j + lr) = acc[i][j][r];
       }
       __syncthreads();
     }
+    // The half is processed in chunks of 8 consecutive elements.  Direct passes: a chunk is
+    // 8 columns of one row, consecutive lanes take consecutive chunks of a row.  Mirror
+    // passes: a chunk is 8 rows of one column, written as 8 consecutive columns of the
+    // transposed output; consecutive lanes take consecutive row chunks of a column.  Full
+    // chunks use one 16-byte (bf16) or 32-byte (fp32) access; chunks that cross the
+    // diagonal or an edge fall back to single elements.
+    constexpr int kRowChunks = kTile / 8;   // chunks per row of the half (32)
+    constexpr int kColChunks = 128 / 8;     // chunks per column of the half (16)
+    constexpr int kChunksHalf = 128 * kRowChunks;
     if (g.tri) {
-      // Direct store of the elements on or below the diagonal: row hr0 + rr, 4 columns.
-      for (int idx = tid; idx < 128 * (kTile / 4); idx += kThreads) {
-        const int rr = idx / (kTile / 4);
-        const int cc = (idx % (kTile / 4)) * 4;
-        const int gi = hr0 + rr;
-        if (gi >= m) continue;
+      for (int idx = tid; idx < kChunksHalf; idx += kThreads) {
+        const int rr = idx / kRowChunks, cc = (idx % kRowChunks) * 8;
+        const int gi = hr0 + rr, gj = col0 + cc;
+        if (gi >= m || gi < gj) continue;  // row invalid, or the chunk lies above the diagonal
+        if (gi >= gj + 7 && gj + 7 < m) {
+          Vec8<S> e8, out;
+          if (kind == kOpPoly) load8(E + int64_t(gi) * lde + gj, e8);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int gj = col0 + cc + e;
-          if (gi < gj || gj >= cstore) continue;
-          const float x = ident ? 0.0f : ep[rr * kEpLd + cc + e];
-          Cp[int64_t(gi) * ldc + gj] =
-              from_f(tri_value(kind, gi, gj, m, x, alpha, E, lde, gi, gj, pa, pb, pc),
-                     static_cast<S*>(nullptr));
+          for (int e = 0; e < 8; ++e) {
+            const float x = ident ? 0.0f : ep_at(rr, cc + e);
+            float val;
+            if (kind == kOpSyrk) val = alpha * x;
+            else if (kind == kOpPoly) val = (gi == gj + e ? pa : 0.0f) + pb * to_f(e8.v[e]) + pc * x;
+            else if (kind == kOpIdent) val = gi == gj + e ? 1.0f : 0.0f;
+            else val = x;
+            out.v[e] = from_f(val, static_cast<S*>(nullptr));
+          }
+          store8(Cp + int64_t(gi) * ldc + gj, out);
+        } else {
+          for (int e = 0; e < 8; ++e) {
+            const int gje = gj + e;
+            if (gi < gje || gje >= cstore) continue;
+            const float x = ident ? 0.0f : ep_at(rr, cc + e);
+            Cp[int64_t(gi) * ldc + gje] =
+                from_f(tri_value(kind, gi, gje, m, x, alpha, E, lde, gi, gje, pa, pb, pc), static_cast<S*>(nullptr));
+          }
         }
       }
-      // Mirrored store of the elements strictly below the diagonal: row gj of C gets
-      // columns hr0 + rr .. hr0 + rr + 3.
-      for (int idx = tid; idx < kTile * 32; idx += kThreads) {
-        const int cc = idx / 32;          // tile column -> row of C
-        const int rr = (idx % 32) * 4;    // 4 consecutive tile rows -> columns of C
-        const int gj = col0 + cc;
-        if (gj >= m) continue;
+      for (int idx = tid; idx < kChunksHalf; idx += kThreads) {
+        const int rr = (idx % kColChunks) * 8, cc = idx / kColChunks;
+        const int gi = hr0 + rr, gj = col0 + cc;
+        if (gj >= m || gi + 7 <= gj) continue;  // row of C invalid, or chunk on/above diagonal
+        if (gi > gj && gi + 7 < m) {
+          Vec8<S> e8, out;
+          if (kind == kOpPoly) load8(E + int64_t(gj) * lde + gi, e8);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int gi = hr0 + rr + e;
-          if (gi <= gj || gi >= cstore) continue;
-          const float x = ident ? 0.0f : ep[(rr + e) * kEpLd + cc];
-          Cp[int64_t(gj) * ldc + gi] =
-              from_f(tri_value(kind, gi, gj, m, x, alpha, E, lde, gj, gi, pa, pb, pc),
-                     static_cast<S*>(nullptr));
+          for (int e = 0; e < 8; ++e) {
+            const float x = ident ? 0.0f : ep_at(rr + e, cc);
+            float val;
+            if (kind == kOpSyrk) val = alpha * x;
+            else if (kind == kOpPoly) val = pb * to_f(e8.v[e]) + pc * x;  // off-diagonal: no pa
+            else if (kind == kOpIdent) val = 0.0f;
+            else val = x;
+            out.v[e] = from_f(val, static_cast<S*>(nullptr));
+          }
+          store8(Cp + int64_t(gj) * ldc + gi, out);
+        } else {
+          for (int e = 0; e < 8; ++e) {
+            const int gie = gi + e;
+            if (gie <= gj || gie >= cstore) continue;
+            const float x = ident ? 0.0f : ep_at(rr + e, cc);
+            Cp[int64_t(gj) * ldc + gie] =
+                from_f(tri_value(kind, gie, gj, m, x, alpha, E, lde, gj, gie, pa, pb, pc), static_cast<S*>(nullptr));
+          }
         }
       }
     } else if (kind == kOpXform) {
+      // Row form C (rows < C.rows, columns < C.kpad, zero beyond cols_out) and its
+      // transpose C2 (rows < C2.rows, columns < C2.kpad, zero beyond rows_out).  Both
+      // leading dimensions are multiples of 8, so chunks never straddle the padding edge.
       const BufDesc C2 = d.buf[g.c2];
       S* C2p = static_cast<S*>(C2.ptr);
-      for (int idx = tid; idx < 128 * (kTile / 4); idx += kThreads) {
-        const int rr = idx / (kTile / 4);
-        const int cc = (idx % (kTile / 4)) * 4;
-        const int gi = hr0 + rr;
-        if (gi >= C.rows) continue;
+      for (int idx = tid; idx < kChunksHalf; idx += kThreads) {
+        const int rr = idx / kRowChunks, cc = (idx % kRowChunks) * 8;
+        const int gi = hr0 + rr, gj = col0 + cc;
+        if (gi >= C.rows || gj >= C.kpad) continue;
+        Vec8<S> out;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int gj = col0 + cc + e;
-          if (gj >= C.kpad) continue;
-          Cp[int64_t(gi) * ldc + gj] =
-              from_f(gj < cols_out ? alpha * ep[rr * kEpLd + cc + e] : 0.0f, static_cast<S*>(nullptr));
-        }
+        for (int e = 0; e < 8; ++e)
+          out.v[e] = from_f(gj + e < cols_out ? alpha * ep_at(rr, cc + e) : 0.0f, static_cast<S*>(nullptr));
+        store8(Cp + int64_t(gi) * ldc + gj, out);
       }
-      for (int idx = tid; idx < kTile * 32; idx += kThreads) {
-        const int cc = idx / 32;
-        const int rr = (idx % 32) * 4;
-        const int gj = col0 + cc;
-        if (gj >= C2.rows) continue;
+      for (int idx = tid; idx < kChunksHalf; idx += kThreads) {
+        const int rr = (idx % kColChunks) * 8, cc = idx / kColChunks;
+        const int gi = hr0 + rr, gj = col0 + cc;
+        if (gj >= C2.rows || gi >= C2.kpad) continue;
+        Vec8<S> out;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int gi = hr0 + rr + e;
-          if (gi >= C2.kpad) continue;
-          C2p[int64_t(gj) * C2.ld + gi] =
-              from_f(gi < rows_out ? alpha * ep[(rr + e) * kEpLd + cc] : 0.0f, static_cast<S*>(nullptr));
-        }
+        for (int e = 0; e < 8; ++e)
+          out.v[e] = from_f(gi + e < rows_out ? alpha * ep_at(rr + e, cc) : 0.0f, static_cast<S*>(nullptr));
+        store8(C2p + int64_t(gj) * C2.ld + gi, out);
       }
     } else {  // kOpUpdate: W -= eta * alpha * (A B^T)
       const float step = d.eta * alpha;
-      for (int idx = tid; idx < 128 * (kTile / 4); idx += kThreads) {
-        const int rr = idx / (kTile / 4);
-        const int cc = (idx % (kTile / 4)) * 4;
-        const int gi = hr0 + rr;
-        if (gi >= rows_out) continue;
+      for (int idx = tid; idx < kChunksHalf; idx += kThreads) {
+        const int rr = idx / kRowChunks, cc = (idx % kRowChunks) * 8;
+        const int gi = hr0 + rr, gj = col0 + cc;
+        if (gi >= rows_out || gj >= cols_out) continue;
+        S* p = Cp + int64_t(gi) * ldc + gj;
+        if (d.wvec && gj + 7 < cols_out) {
+          Vec8<S> w;
+          load8(p, w);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int gj = col0 + cc + e;
-          if (gj >= cols_out) continue;
-          S* p = Cp + int64_t(gi) * ldc + gj;
-          *p = from_f(fmaf(-step, ep[rr * kEpLd + cc + e], to_f(*p)), static_cast<S*>(nullptr));
+          for (int e = 0; e < 8; ++e)
+            w.v[e] = from_f(fmaf(-step, ep_at(rr, cc + e), to_f(w.v[e])), static_cast<S*>(nullptr));
+          store8(p, w);
+        } else {
+          for (int e = 0; e < 8 && gj + e < cols_out; ++e)
+            p[e] = from_f(fmaf(-step, ep_at(rr, cc + e), to_f(p[e])), static_cast<S*>(nullptr));
         }
       }
     }
@@ -346,4 +593,19 @@ int muon_launch_gemm(const GemmArgs& a, int dtype, void* stream) {
   else
     hipLaunchKernelGGL(k_gemm<float>, dim3(a.total_tiles), dim3(kThreads), 0, s, a);
   return hipGetLastError();
+}
+
+// Test hooks for host-side checks of tile_order.h.
+extern "C" int muon_debug_xcd_remap(int total, int* out) {
+  for (int w = 0; w < total; ++w) out[w] = xcd_remap(w, total);
+  return total;
+}
+
+extern "C" int muon_debug_tile_order(int tri, int tm, int tn, int* ti, int* tj) {
+  const int n = tri ? tm * (tm + 1) / 2 : tm * tn;
+  for (int t = 0; t < n; ++t) {
+    if (tri) tri_band_decode(t, tm, ti[t], tj[t]);
+    else full_band_decode(t, tm, tn, ti[t], tj[t]);
+  }
+  return n;
 }

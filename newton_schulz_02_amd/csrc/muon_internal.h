@@ -2,12 +2,12 @@
 //
 // Data layout in HBM (all row-major):
 //   - caller buffers: W, G, M are rows x cols with leading dimension cols;
-//   - per matrix, m = min(rows, cols), n = max(rows, cols), mp = round_up(m, 64),
-//     np = round_up(n, 64);
+//   - per matrix, m = min(rows, cols), n = max(rows, cols), mp = round_up(m, 128),
+//     np = round_up(n, 128);
 //   - Gram slots (5 per matrix): m rows x mp columns, columns m..mp-1 held at zero so a
 //     contraction may always run over mp;
 //   - row form X (m x np) and transposed form X^T (n x mp), zero padded the same way.
-//     When the caller's momentum buffer already has a 64-multiple leading dimension and
+//     When the caller's momentum buffer already has a 128-multiple leading dimension and
 //     16-byte alignment it is used in place as one of the two forms.
 #pragma once
 
@@ -16,7 +16,7 @@
 namespace muon {
 
 constexpr int kTile = 256;       // output tile edge of the MFMA kernels (both dtypes)
-constexpr int kKPad = 64;        // contraction dimensions are padded to this multiple
+constexpr int kKPad = 128;       // contraction dimensions are padded to this multiple
 constexpr int kEwTile = 64;      // tile edge of the momentum/transpose kernel
 constexpr int kMaxGroups = 8;    // op groups per grouped GEMM launch
 constexpr int kSlots = 5;        // m x m Gram buffers per matrix
@@ -58,14 +58,16 @@ struct MatDesc {
   BufDesc buf[kNumBuf];
   const void* grad;      // caller G (rows x cols)
   void* mom;             // caller M (rows x cols), updated in place
-  void* copy_out;        // padded same-orientation copy of M' (rows x round_up(cols,64)) or null
-  void* trans_out;       // transposed copy of M' (cols x round_up(rows,64)) or null
+  void* copy_out;        // padded same-orientation copy of M' (rows x round_up(cols,kKPad)) or null
+  void* trans_out;       // transposed copy of M' (cols x round_up(rows,kKPad)) or null
   int64_t copy_ld;
   int64_t trans_ld;
   int32_t rows, cols;
-  int32_t vec;           // caller rows are 16-byte aligned: vector access allowed
+  int32_t vec;           // rows of G and M are 16-byte aligned: vector access allowed
+  int32_t wvec;          // rows of W are 16-byte aligned: vector access allowed
   int32_t mom_prefix;    // first momentum tile of this matrix (all matrices, sorted order)
-  int32_t mom_tiles_c;   // momentum tiles along cols
+  int32_t mom_tiles_c;   // momentum tiles along cols (cover round_up(cols, kKPad))
+  int32_t mom_tiles_r;   // momentum tiles along rows (cover round_up(rows, kKPad))
   int32_t tri_prefix;    // first lower-triangle GEMM tile (prefix over sorted order)
   int32_t full_prefix;   // first full GEMM tile (prefix over sorted order)
   float eta;             // lr * sqrt(max(1, rows/cols))

@@ -309,8 +309,11 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
     }
     p.tri_tiles = tri_tiles_of(p.m);
     p.full_tiles = full_tiles_of(p.m, p.n);
-    p.mom_tiles_c = ceil_div(p.c, kEwTile);
-    p.mom_tiles = ceil_div(p.r, kEwTile) * p.mom_tiles_c;
+    // Momentum tiles cover the extents rounded up to kKPad, so that the zero padding of the
+    // row and transposed copies (leading dimensions rounded to kKPad) is written too.
+    p.mom_tiles_c = round_up(p.c, kKPad) / kEwTile;
+    p.mom_tiles_r = round_up(p.r, kKPad) / kEwTile;
+    p.mom_tiles = p.mom_tiles_r * p.mom_tiles_c;
     p.tri_prefix = tri;
     p.full_prefix = full;
     p.mom_prefix = mom;
@@ -466,6 +469,7 @@ void fill_descs(const Plan& plan, const muon_matrix* mats, const muon_hparams* h
              (p.c * es) % 16 == 0)
                 ? 1
                 : 0;
+    d.wvec = ((uintptr_t)x.param % 16 == 0 && (p.c * es) % 16 == 0) ? 1 : 0;
     const bool caller_ok = (p.c % kKPad == 0) && ((uintptr_t)x.momentum % 16 == 0);
     for (int s = 0; s < kSlots; ++s)
       d.buf[kSlot0 + s] = {at(kSlot0 + s), p.mp, int32_t(p.m), int32_t(p.mp)};
@@ -502,6 +506,7 @@ void fill_descs(const Plan& plan, const muon_matrix* mats, const muon_hparams* h
     d.buf[kW] = {x.param, p.c, int32_t(p.r), 0};
     d.mom_prefix = int32_t(p.mom_prefix);
     d.mom_tiles_c = int32_t(p.mom_tiles_c);
+    d.mom_tiles_r = int32_t(p.mom_tiles_r);
     d.tri_prefix = int32_t(p.tri_prefix);
     d.full_prefix = int32_t(p.full_prefix);
     d.eta = float(double(hp->lr) * std::sqrt(std::max(1.0, double(p.r) / double(p.c))));

@@ -31,7 +31,7 @@ struct PlanMat {
   int64_t off[kNumBuf];          // workspace offsets of workspace-resident buffers, -1 if none
   int64_t copy_off = -1;         // reserved padded same-orientation copy
   int64_t trans_off = -1;        // reserved transposed copy
-  int64_t tri_tiles = 0, full_tiles = 0, mom_tiles = 0, mom_tiles_c = 0;
+  int64_t tri_tiles = 0, full_tiles = 0, mom_tiles = 0, mom_tiles_c = 0, mom_tiles_r = 0;
   int64_t tri_prefix = 0, full_prefix = 0, mom_prefix = 0;
   double flops = 0, bytes = 0;
 };

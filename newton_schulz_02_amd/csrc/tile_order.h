@@ -1,0 +1,63 @@
+// Tile orders of the grouped MFMA kernel, shared by the kernel and a host-side test hook.
+//
+// 1. XCD remap.  MI355X has 8 XCDs, each with its own L2; the dispatcher sends workgroup w
+//    to XCD (w mod 8).  xcd_remap() renumbers workgroups so that XCD x receives one
+//    contiguous range of logical tiles, so tiles that share operand panels share an L2.
+// 2. Banded order inside one matrix.  Tile rows are grouped in bands of kBand rows and a
+//    band is walked column by column, so consecutive tiles reuse the same kBand A panels
+//    and step through B panels one at a time.  tri_band_decode() does this over the lower
+//    triangle (ti >= tj), full_band_decode() over a full TM x TN grid.
+#pragma once
+
+#ifdef __HIPCC__
+#define MUON_HD __host__ __device__ __forceinline__
+#else
+#define MUON_HD inline
+#endif
+
+namespace muon {
+
+constexpr int kXcds = 8;
+constexpr int kBand = 4;
+
+// Logical tile index of workgroup w in a grid of `total` workgroups.
+MUON_HD int xcd_remap(int w, int total) {
+  const int q = total / kXcds, r = total % kXcds;
+  const int x = w % kXcds, i = w / kXcds;
+  return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// t in [0, T(T+1)/2) -> (ti, tj), ti >= tj, for a T x T tile grid.
+// Band s (rows 4s .. 4s+h-1, h = min(4, T-4s)) holds 4s*h tiles left of the diagonal block,
+// walked column-major, then the h(h+1)/2 tiles of its diagonal block, column by column.
+// Full bands before band s hold 8 s^2 + 2 s tiles.
+MUON_HD void tri_band_decode(int t, int T, int& ti, int& tj) {
+  int s = 0;
+  while (8 * (s + 1) * (s + 1) + 2 * (s + 1) <= t && 4 * (s + 1) < T) ++s;
+  int u = t - (8 * s * s + 2 * s);
+  const int h = (T - 4 * s) < kBand ? (T - 4 * s) : kBand;
+  if (u < 4 * s * h) {
+    tj = u / h;
+    ti = 4 * s + u % h;
+  } else {
+    int v = u - 4 * s * h;
+    int c = 0;
+    while (v >= h - c) {
+      v -= h - c;
+      ++c;
+    }
+    tj = 4 * s + c;
+    ti = 4 * s + c + v;
+  }
+}
+
+// t in [0, TM*TN) -> (ti, tj): bands of kBand tile rows, each walked column-major.
+MUON_HD void full_band_decode(int t, int TM, int TN, int& ti, int& tj) {
+  const int s = t / (kBand * TN);
+  const int u = t - s * kBand * TN;
+  const int h = (TM - kBand * s) < kBand ? (TM - kBand * s) : kBand;
+  tj = u / h;
+  ti = kBand * s + u % h;
+}
+
+}  // namespace muon

@@ -242,3 +242,30 @@ def test_workspace_size_independent_of_pointers_and_grows_with_count():
     assert s1 == nm.workspace_size_raw(a2, 1, HP)
     assert nm.workspace_size_raw(nm.shape_array([(300, 700)] * 2), 2, HP) > s1
     assert s1 % 256 == 0
+
+
+# --- tile orders of the MFMA kernel --------------------------------------------------------
+
+@pytest.mark.parametrize("T", list(range(1, 20)) + [43, 64])
+def test_triangle_order_is_a_bijection_onto_the_lower_triangle(T):
+    order = nm.tile_order(True, T)
+    assert len(order) == T * (T + 1) // 2
+    assert sorted(order) == sorted((i, j) for i in range(T) for j in range(i + 1))
+    # Banded: the first tiles stay within the first band of 4 tile rows.
+    assert all(i < 4 for i, _ in order[:min(10, len(order))])
+
+
+@pytest.mark.parametrize("TM,TN", [(1, 1), (1, 7), (5, 3), (16, 43), (43, 16), (9, 9)])
+def test_full_order_is_a_bijection(TM, TN):
+    order = nm.tile_order(False, TM, TN)
+    assert sorted(order) == sorted((i, j) for i in range(TM) for j in range(TN))
+
+
+@pytest.mark.parametrize("total", [1, 5, 8, 9, 136, 952, 1001, 3088])
+def test_xcd_remap_is_a_permutation_with_contiguous_xcd_ranges(total):
+    out = nm.xcd_remap(total)
+    assert sorted(out) == list(range(total))
+    # Workgroups dispatched to one XCD (w mod 8) cover one contiguous logical range.
+    for x in range(8):
+        mine = sorted(out[w] for w in range(x, total, 8))
+        assert mine == list(range(mine[0], mine[0] + len(mine))) if mine else True
