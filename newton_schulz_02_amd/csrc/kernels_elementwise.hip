@@ -45,13 +45,19 @@ struct Chunk {
   S v[N];
 };
 
+// 16-byte global accesses through address-space-1 pointers: the buffer pointers come from
+// the descriptor table (generic), and FLAT accesses would also hold up the LDS waits.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) u32x4* g_u32x4;
+typedef __attribute__((address_space(1))) const u32x4* g_cu32x4;
+
 template <typename S>
 __device__ __forceinline__ void load_chunk(const S* p, Chunk<S>& c) {
-  *reinterpret_cast<uint4*>(c.v) = *reinterpret_cast<const uint4*>(p);
+  *reinterpret_cast<u32x4*>(c.v) = *(g_cu32x4)(p);
 }
 template <typename S>
 __device__ __forceinline__ void store_chunk(S* p, const Chunk<S>& c) {
-  *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(c.v);
+  *(g_u32x4)(p) = *reinterpret_cast<const u32x4*>(c.v);
 }
 
 template <typename S>

@@ -53,6 +53,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kThreads = 512;
@@ -73,9 +75,10 @@ constexpr int kInstPerOperand = kOperandBytes / 1024 / kWaves;  // per wave per 
 constexpr int kEpW = kTile / kStages;
 constexpr int kEpArrBytes = 128 * kEpLd * 4;
 // bf16 outputs of the Gram products and re-anchors are staged once, transposed: T-row c
-// (a tile column) holds the 256 tile rows; T-rows 0..127 in lds0, 128..255 in lds1.
+// (a tile column) holds the 256 tile rows; the T-rows are split evenly over the arrays.
 constexpr int kTs = kTile + 8;                 // bf16 T-row stride (528 bytes: 16-byte aligned)
-constexpr int kTArrBytes = 128 * kTs * 2;
+constexpr int kTRowsPerArr = kTile / kStages;
+constexpr int kTArrBytes = kTRowsPerArr * kTs * 2;
 constexpr int kMaxAB = kStageBytes > kEpArrBytes ? kStageBytes : kEpArrBytes;
 constexpr int kArrBytes = kMaxAB > kTArrBytes ? kMaxAB : kTArrBytes;
 static_assert(kRowBytes == 128 || kRowBytes == 64, "row bytes per stage");
@@ -152,35 +155,39 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Global-memory pointers.  Pointers read from the descriptor table are generic; accesses
+// through them would compile to FLAT instructions, which may alias LDS, so every wait for
+// an LDS access would also wait for them.  The epilogue casts to address space 1 instead.
+template <typename T>
+using gptr = __attribute__((address_space(1))) T*;
+template <typename T>
+__device__ __forceinline__ gptr<T> to_global(T* p) {
+  return (gptr<T>)(p);
+}
+
 // Eight consecutive elements of S as one 16- or 32-byte vector.
 template <typename S>
 struct Vec8 {
   S v[8];
 };
 template <typename S>
-__device__ __forceinline__ void load8(const S* p, Vec8<S>& x) {
-  if constexpr (sizeof(S) == 2) {
-    *reinterpret_cast<uint4*>(x.v) = *reinterpret_cast<const uint4*>(p);
-  } else {
-    reinterpret_cast<uint4*>(x.v)[0] = reinterpret_cast<const uint4*>(p)[0];
-    reinterpret_cast<uint4*>(x.v)[1] = reinterpret_cast<const uint4*>(p)[1];
-  }
+__device__ __forceinline__ void load8(gptr<const S> p, Vec8<S>& x) {
+  const gptr<const u32x4> q = (gptr<const u32x4>)p;
+  reinterpret_cast<u32x4*>(x.v)[0] = q[0];
+  if constexpr (sizeof(S) == 4) reinterpret_cast<u32x4*>(x.v)[1] = q[1];
 }
 template <typename S>
-__device__ __forceinline__ void store8(S* p, const Vec8<S>& x) {
-  if constexpr (sizeof(S) == 2) {
-    *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(x.v);
-  } else {
-    reinterpret_cast<uint4*>(p)[0] = reinterpret_cast<const uint4*>(x.v)[0];
-    reinterpret_cast<uint4*>(p)[1] = reinterpret_cast<const uint4*>(x.v)[1];
-  }
+__device__ __forceinline__ void store8(gptr<S> p, const Vec8<S>& x) {
+  const gptr<u32x4> q = (gptr<u32x4>)p;
+  q[0] = reinterpret_cast<const u32x4*>(x.v)[0];
+  if constexpr (sizeof(S) == 4) q[1] = reinterpret_cast<const u32x4*>(x.v)[1];
 }
 
 // Value of the symmetric-output epilogues at (gi, gj); x is the accumulated product.  E is
 // read at (er, ec), which is (gi, gj) or its mirror: stored iterates are exactly symmetric.
 template <typename S>
 __device__ __forceinline__ float tri_value(int kind, int gi, int gj, int m, float x, float alpha,
-                                           const S* E, int64_t lde, int er, int ec, float pa,
+                                           gptr<const S> E, int64_t lde, int er, int ec, float pa,
                                            float pb, float pc) {
   if (gi >= m || gj >= m) return 0.0f;
   if (kind == kOpSyrk) return alpha * x;
@@ -288,7 +295,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
     }
   };
   constexpr int kLoadsPerStage = 2 * kInstPerOperand;
-
   // Prologue: stages 0 .. kStages-2 in flight.
   static_for<0, kStages - 1>([&](auto sc) {
     if (sc.value < ksteps) issue(sc.value, stage_of(sc));
@@ -297,6 +303,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
   // Fragment rows of this lane (+ 32 i for A, + 32 j for B).
   const int a_row = wm * 128 + lr;
   const int b_row = wn * 64 + lr;
+  constexpr int kKK = kRowBytes / 32;  // MFMA k-blocks per step
+  // Fragments of k-block kk (16-byte chunk 2 kk + lk of the lane's rows) from stage st.
+  auto load_frags = [&](const char* st, int kk, uint4* fa, uint4* fb) {
+    const int c = 2 * kk + lk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = a_row + 32 * i;
+      fa[i] = *reinterpret_cast<const uint4*>(st + r * kRowBytes + ((c ^ swz(r)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < kFragN; ++j) {
+      const int r = b_row + 32 * j;
+      fb[j] = *reinterpret_cast<const uint4*>(st + kOperandBytes + r * kRowBytes + ((c ^ swz(r)) << 4));
+    }
+  };
   // One k-step: wait until this wave's loads of stage ks landed (at most `pending` newer
   // loads remain), barrier, issue the loads kStages-1 steps ahead, run the MFMAs.
   auto kstep = [&](int ks, auto sc, auto pending) {
@@ -304,28 +325,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
     stage_barrier();  // all waves' loads of stage ks landed; stage ks-1 is free again
     if (ks + kStages - 1 < ksteps)
       issue(ks + kStages - 1, stage_of(std::integral_constant<int, decltype(sc)::value + kStages - 1>{}));
-    if (!idle) {
-      const char* st = stage_of(sc);
+    if (idle) return;
+    const char* st = stage_of(sc);
 #pragma unroll
-      for (int kk = 0; kk < kRowBytes / 32; ++kk) {
-        const int c = 2 * kk + lk;   // 16-byte chunk of this lane's 8 (or 4) k values
-        uint4 fa[4], fb[kFragN];
+    for (int kk = 0; kk < kKK; ++kk) {
+      uint4 fa[4], fb[kFragN];
+      load_frags(st, kk, fa, fb);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = a_row + 32 * i;
-          fa[i] = *reinterpret_cast<const uint4*>(st + r * kRowBytes + ((c ^ swz(r)) << 4));
-        }
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < kFragN; ++j) {
-          const int r = b_row + 32 * j;
-          fb[j] = *reinterpret_cast<const uint4*>(st + kOperandBytes + r * kRowBytes +
-                                                  ((c ^ swz(r)) << 4));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < kFragN; ++j) Mma<S>::step(fa[i], fb[j], acc[i][j]);
-      }
+        for (int j = 0; j < kFragN; ++j) Mma<S>::step(fa[i], fb[j], acc[i][j]);
     }
   };
   // ksteps is a multiple of kStages (contraction dims are padded to kKPad).  Full blocks
@@ -350,9 +359,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
   float alpha = 1.0f;
   if (g.alpha == kAlphaS) alpha = args.scale[lo];
   else if (g.alpha == kAlphaS2) alpha = args.scale[lo] * args.scale[lo];
-  S* Cp = static_cast<S*>(C.ptr);
+  const gptr<S> Cp = to_global(static_cast<S*>(C.ptr));
   const int64_t ldc = C.ld;
-  const S* E = g.e >= 0 ? static_cast<const S*>(d.buf[g.e].ptr) : nullptr;
+  const gptr<const S> E = to_global(static_cast<const S*>(g.e >= 0 ? d.buf[g.e].ptr : C.ptr));
   const int64_t lde = g.e >= 0 ? d.buf[g.e].ld : 0;
   const float pa = args.pa, pb = args.pb, pc = args.pc;
   const int m = rows_out;    // symmetric outputs: valid rows/cols
@@ -365,12 +374,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
   if constexpr (sizeof(S) == 2) {
     if (kind != kOpUpdate) {
       auto t_row = [&](int c) -> uint16_t* {
-        return reinterpret_cast<uint16_t*>(c < 128 ? lds0 : lds1) + (c & 127) * kTs;
+        const int q = c / kTRowsPerArr;
+        char* base = q == 0 ? lds0 : q == 1 ? lds1 : q == 2 ? lds2 : lds3;
+        return reinterpret_cast<uint16_t*>(base) + (c % kTRowsPerArr) * kTs;
       };
       const bool xform = kind == kOpXform;
-      if (!above) {
+      // Stage the wave's values; K is the op kind as a compile-time constant.
+      auto stage = [&](auto kc) {
+        constexpr int K = decltype(kc)::value;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          // The polynomial's iterate: E[gj][gi0 .. gi0+3] = E[gi0 .. gi0+3][gj], 8 bytes per
+          // (j, r4); all 8 loads of this i are issued before any is used.
+          u32x2 e4[kFragN][4];
+          if constexpr (K == kOpPoly) {
+#pragma unroll
+            for (int j = 0; j < kFragN; ++j)
+#pragma unroll
+              for (int r4 = 0; r4 < 4; ++r4) {
+                const int gi0 = row0 + 128 * wm + 32 * i + 8 * r4 + 4 * lk;
+                const int gj = col0 + 64 * wn + 32 * j + lr;
+                e4[j][r4] = u32x2{0u, 0u};
+                if (gj < m && gi0 < m) e4[j][r4] = *(gptr<const u32x2>)(E + int64_t(gj) * lde + gi0);
+              }
+          }
 #pragma unroll
           for (int j = 0; j < kFragN; ++j)
 #pragma unroll
@@ -378,32 +405,42 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
               const int lrow = 128 * wm + 32 * i + 8 * r4 + 4 * lk;  // 4 rows lrow .. lrow+3
               const int lcol = 64 * wn + 32 * j + lr;
               const int gi0 = row0 + lrow, gj = col0 + lcol;
-              uint2 e4 = make_uint2(0, 0);
-              if (kind == kOpPoly && gj < m && gi0 < m)
-                e4 = *reinterpret_cast<const uint2*>(E + int64_t(gj) * lde + gi0);
-              const uint16_t* ev = reinterpret_cast<const uint16_t*>(&e4);
               uint16_t o[4];
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
                 const int gi = gi0 + q;
                 const float x = acc[i][j][4 * r4 + q];
-                float val = 0.0f;
-                if (xform) {
-                  if (gi < rows_out && gj < cols_out) val = alpha * x;
-                } else if (gi < m && gj < m) {
-                  if (kind == kOpSyrk) val = alpha * x;
-                  else if (kind == kOpPoly) val = (gi == gj ? pa : 0.0f) + pb * to_f(ev[q]) + pc * x;
-                  else if (kind == kOpIdent) val = gi == gj ? 1.0f : 0.0f;
-                  else val = x;
+                float val;
+                if constexpr (K == kOpXform) {
+                  val = (gi < rows_out && gj < cols_out) ? alpha * x : 0.0f;
+                } else {
+                  const bool in = gi < m && gj < m;
+                  if constexpr (K == kOpSyrk) val = in ? alpha * x : 0.0f;
+                  else if constexpr (K == kOpPoly)
+                    val = in ? (gi == gj ? pa : 0.0f) +
+                                   pb * to_f(reinterpret_cast<const uint16_t*>(&e4[j][r4])[q]) + pc * x
+                             : 0.0f;
+                  else if constexpr (K == kOpIdent) val = (in && gi == gj) ? 1.0f : 0.0f;
+                  else val = in ? x : 0.0f;
                 }
                 o[q] = from_f(val, static_cast<uint16_t*>(nullptr));
               }
               *reinterpret_cast<uint2*>(t_row(lcol) + lrow) = *reinterpret_cast<const uint2*>(o);
             }
+        }
+      };
+      if (!above) {
+        switch (kind) {
+          case kOpSyrk: stage(std::integral_constant<int, kOpSyrk>{}); break;
+          case kOpPoly: stage(std::integral_constant<int, kOpPoly>{}); break;
+          case kOpXform: stage(std::integral_constant<int, kOpXform>{}); break;
+          case kOpIdent: stage(std::integral_constant<int, kOpIdent>{}); break;
+          default: stage(std::integral_constant<int, kOpProd>{}); break;
+        }
       }
       __syncthreads();
       // Transposed-side pass: row gj = col0 + c of the output gets tile rows r .. r+7.
-      S* Tp = xform ? static_cast<S*>(d.buf[g.c2].ptr) : Cp;
+      const gptr<S> Tp = xform ? to_global(static_cast<S*>(d.buf[g.c2].ptr)) : Cp;
       const int64_t ldt = xform ? d.buf[g.c2].ld : ldc;
       const int t_rows = xform ? d.buf[g.c2].rows : m;          // valid output rows
       const int t_cols = xform ? d.buf[g.c2].kpad : cstore;     // stored output columns
@@ -446,13 +483,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
     }
   }
 
-  // Staged fp32 value at (row rr of the half, tile column cc).
+  // fp32 path (the update, and every op of the fp32 kernel): the accumulators are staged in
+  // fp32, one 128-row half at a time, split by column block across the stage arrays.
   auto ep_at = [&](int rr, int cc) -> float& {
     const int q = cc / kEpW;
     char* base = q == 0 ? lds0 : q == 1 ? lds1 : q == 2 ? lds2 : lds3;
     return reinterpret_cast<float*>(base)[rr * kEpLd + cc % kEpW];
   };
-
+  // Chunks of 8 consecutive elements.  Direct passes: 8 columns of one row, consecutive lanes
+  // on consecutive chunks of a row.  Mirror passes: 8 rows of one column, written as 8
+  // consecutive columns of the transposed output, consecutive lanes on consecutive row
+  // chunks.  Full chunks use one 16- or 32-byte access; chunks that cross the diagonal or an
+  // edge fall back to single elements.
+  constexpr int kRowChunks = kTile / 8;   // chunks per row of a half (32)
+  constexpr int kColChunks = 128 / 8;     // chunks per column of a half (16)
+  constexpr int kChunksHalf = 128 * kRowChunks;
   for (int half = 0; half < 2; ++half) {
     const int hr0 = row0 + half * 128;  // first row of this half
     if (!ident) {
@@ -467,23 +512,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
       }
       __syncthreads();
     }
-    // The half is processed in chunks of 8 consecutive elements.  Direct passes: a chunk is
-    // 8 columns of one row, consecutive lanes take consecutive chunks of a row.  Mirror
-    // passes: a chunk is 8 rows of one column, written as 8 consecutive columns of the
-    // transposed output; consecutive lanes take consecutive row chunks of a column.  Full
-    // chunks use one 16-byte (bf16) or 32-byte (fp32) access; chunks that cross the
-    // diagonal or an edge fall back to single elements.
-    constexpr int kRowChunks = kTile / 8;   // chunks per row of the half (32)
-    constexpr int kColChunks = 128 / 8;     // chunks per column of the half (16)
-    constexpr int kChunksHalf = 128 * kRowChunks;
-    if (g.tri) {
+    if (kind == kOpUpdate) {  // W -= eta * alpha * (A B^T)
+      const float step = d.eta * alpha;
+      for (int idx = tid; idx < kChunksHalf; idx += kThreads) {
+        const int rr = idx / kRowChunks, cc = (idx % kRowChunks) * 8;
+        const int gi = hr0 + rr, gj = col0 + cc;
+        if (gi >= rows_out || gj >= cols_out) continue;
+        const gptr<S> p = Cp + int64_t(gi) * ldc + gj;
+        if (d.wvec && gj + 7 < cols_out) {
+          Vec8<S> w;
+          load8<S>(p, w);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            w.v[e] = from_f(fmaf(-step, ep_at(rr, cc + e), to_f(w.v[e])), static_cast<S*>(nullptr));
+          store8(p, w);
+        } else {
+          for (int e = 0; e < 8 && gj + e < cols_out; ++e)
+            p[e] = from_f(fmaf(-step, ep_at(rr, cc + e), to_f(p[e])), static_cast<S*>(nullptr));
+        }
+      }
+    } else if (g.tri) {
       for (int idx = tid; idx < kChunksHalf; idx += kThreads) {
         const int rr = idx / kRowChunks, cc = (idx % kRowChunks) * 8;
         const int gi = hr0 + rr, gj = col0 + cc;
         if (gi >= m || gi < gj) continue;  // row invalid, or the chunk lies above the diagonal
         if (gi >= gj + 7 && gj + 7 < m) {
           Vec8<S> e8, out;
-          if (kind == kOpPoly) load8(E + int64_t(gi) * lde + gj, e8);
+          if (kind == kOpPoly) load8<S>(E + int64_t(gi) * lde + gj, e8);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float x = ident ? 0.0f : ep_at(rr, cc + e);
@@ -501,7 +556,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
             if (gi < gje || gje >= cstore) continue;
             const float x = ident ? 0.0f : ep_at(rr, cc + e);
             Cp[int64_t(gi) * ldc + gje] =
-                from_f(tri_value(kind, gi, gje, m, x, alpha, E, lde, gi, gje, pa, pb, pc), static_cast<S*>(nullptr));
+                from_f(tri_value<S>(kind, gi, gje, m, x, alpha, E, lde, gi, gje, pa, pb, pc), static_cast<S*>(nullptr));
           }
         }
       }
@@ -511,7 +566,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
         if (gj >= m || gi + 7 <= gj) continue;  // row of C invalid, or chunk on/above diagonal
         if (gi > gj && gi + 7 < m) {
           Vec8<S> e8, out;
-          if (kind == kOpPoly) load8(E + int64_t(gj) * lde + gi, e8);
+          if (kind == kOpPoly) load8<S>(E + int64_t(gj) * lde + gi, e8);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float x = ident ? 0.0f : ep_at(rr + e, cc);
@@ -529,16 +584,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
             if (gie <= gj || gie >= cstore) continue;
             const float x = ident ? 0.0f : ep_at(rr + e, cc);
             Cp[int64_t(gj) * ldc + gie] =
-                from_f(tri_value(kind, gie, gj, m, x, alpha, E, lde, gj, gie, pa, pb, pc), static_cast<S*>(nullptr));
+                from_f(tri_value<S>(kind, gie, gj, m, x, alpha, E, lde, gj, gie, pa, pb, pc), static_cast<S*>(nullptr));
           }
         }
       }
-    } else if (kind == kOpXform) {
+    } else {  // kOpXform
       // Row form C (rows < C.rows, columns < C.kpad, zero beyond cols_out) and its
       // transpose C2 (rows < C2.rows, columns < C2.kpad, zero beyond rows_out).  Both
       // leading dimensions are multiples of 8, so chunks never straddle the padding edge.
       const BufDesc C2 = d.buf[g.c2];
-      S* C2p = static_cast<S*>(C2.ptr);
+      const gptr<S> C2p = to_global(static_cast<S*>(C2.ptr));
       for (int idx = tid; idx < kChunksHalf; idx += kThreads) {
         const int rr = idx / kRowChunks, cc = (idx % kRowChunks) * 8;
         const int gi = hr0 + rr, gj = col0 + cc;
@@ -558,25 +613,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
         for (int e = 0; e < 8; ++e)
           out.v[e] = from_f(gi + e < rows_out ? alpha * ep_at(rr + e, cc) : 0.0f, static_cast<S*>(nullptr));
         store8(C2p + int64_t(gj) * C2.ld + gi, out);
-      }
-    } else {  // kOpUpdate: W -= eta * alpha * (A B^T)
-      const float step = d.eta * alpha;
-      for (int idx = tid; idx < kChunksHalf; idx += kThreads) {
-        const int rr = idx / kRowChunks, cc = (idx % kRowChunks) * 8;
-        const int gi = hr0 + rr, gj = col0 + cc;
-        if (gi >= rows_out || gj >= cols_out) continue;
-        S* p = Cp + int64_t(gi) * ldc + gj;
-        if (d.wvec && gj + 7 < cols_out) {
-          Vec8<S> w;
-          load8(p, w);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            w.v[e] = from_f(fmaf(-step, ep_at(rr, cc + e), to_f(w.v[e])), static_cast<S*>(nullptr));
-          store8(p, w);
-        } else {
-          for (int e = 0; e < 8 && gj + e < cols_out; ++e)
-            p[e] = from_f(fmaf(-step, ep_at(rr, cc + e), to_f(p[e])), static_cast<S*>(nullptr));
-        }
       }
     }
     if (!ident) __syncthreads();

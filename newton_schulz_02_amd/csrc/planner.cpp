@@ -412,6 +412,14 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
           if (!joined) groups.push_back({o, i, i + 1});
         }
       }
+      // Longest tiles first (per-tile cost grows with the contraction length), so a launch
+      // does not end on a few long tiles.
+      auto tile_k = [&](const G& g) {
+        const PlanMat& p = plan->mats[g.first];
+        return g.op.kind == kOpSyrk ? p.n : p.m;
+      };
+      std::stable_sort(groups.begin(), groups.end(),
+                       [&](const G& x, const G& y) { return tile_k(x) > tile_k(y); });
       for (size_t g0 = 0; g0 < groups.size(); g0 += kMaxGroups) {
         PlanLaunch L;
         L.kind = kLaunchGemm;
@@ -475,8 +483,10 @@ void fill_descs(const Plan& plan, const muon_matrix* mats, const muon_hparams* h
       d.buf[kSlot0 + s] = {at(kSlot0 + s), p.mp, int32_t(p.m), int32_t(p.mp)};
     const BufDesc row_ws = {at(kXrIn), p.np, int32_t(p.m), int32_t(p.np)};
     const BufDesc t_ws = {at(kXtIn), p.mp, int32_t(p.n), int32_t(p.mp)};
-    d.copy_ld = round_up(p.c, kKPad);
-    d.trans_ld = round_up(p.r, kKPad);
+    // Leading dimensions of the copies the momentum kernel writes: row form (m x np) and
+    // transposed form (n x mp) of X.
+    d.copy_ld = p.tall ? t_ws.ld : row_ws.ld;
+    d.trans_ld = p.tall ? row_ws.ld : t_ws.ld;
     if (!p.tall) {
       // X = M' (m = rows): row form is M' itself or its padded copy; X^T is the transpose.
       if (caller_ok) {

@@ -1,8 +1,11 @@
 // Tile orders of the grouped MFMA kernel, shared by the kernel and a host-side test hook.
 //
-// 1. XCD remap.  MI355X has 8 XCDs, each with its own L2; the dispatcher sends workgroup w
-//    to XCD (w mod 8).  xcd_remap() renumbers workgroups so that XCD x receives one
-//    contiguous range of logical tiles, so tiles that share operand panels share an L2.
+// 1. XCD remap.  MI355X has 8 XCDs (32 CUs each), each with its own L2; the dispatcher
+//    sends workgroup w to XCD (w mod 8).  xcd_remap() deals logical tiles to the XCDs in
+//    chunks of kXcdChunk consecutive tiles, round robin: the tiles one XCD runs at once
+//    are consecutive (they share operand panels in its L2), all XCDs work on the same
+//    window of about 8 * kXcdChunk tiles (whose panels fit the shared last-level cache),
+//    and tiles of different cost are spread over all XCDs.
 // 2. Banded order inside one matrix.  Tile rows are grouped in bands of kBand rows and a
 //    band is walked column by column, so consecutive tiles reuse the same kBand A panels
 //    and step through B panels one at a time.  tri_band_decode() does this over the lower
@@ -18,13 +21,16 @@
 namespace muon {
 
 constexpr int kXcds = 8;
+constexpr int kXcdChunk = 32;
 constexpr int kBand = 4;
 
-// Logical tile index of workgroup w in a grid of `total` workgroups.
+// Logical tile index of workgroup w in a grid of `total` workgroups.  Workgroups past the
+// last whole round of kXcds chunks keep their own index.
 MUON_HD int xcd_remap(int w, int total) {
-  const int q = total / kXcds, r = total % kXcds;
+  const int round = kXcds * kXcdChunk;
+  if (w >= total / round * round) return w;
   const int x = w % kXcds, i = w / kXcds;
-  return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+  return (i / kXcdChunk) * round + x * kXcdChunk + i % kXcdChunk;
 }
 
 // t in [0, T(T+1)/2) -> (ti, tj), ti >= tj, for a T x T tile grid.

@@ -261,11 +261,15 @@ def test_full_order_is_a_bijection(TM, TN):
     assert sorted(order) == sorted((i, j) for i in range(TM) for j in range(TN))
 
 
-@pytest.mark.parametrize("total", [1, 5, 8, 9, 136, 952, 1001, 3088])
-def test_xcd_remap_is_a_permutation_with_contiguous_xcd_ranges(total):
+@pytest.mark.parametrize("total", [1, 5, 8, 9, 136, 256, 952, 1001, 3088])
+def test_xcd_remap_is_a_permutation_dealing_chunks_round_robin(total):
     out = nm.xcd_remap(total)
     assert sorted(out) == list(range(total))
-    # Workgroups dispatched to one XCD (w mod 8) cover one contiguous logical range.
-    for x in range(8):
-        mine = sorted(out[w] for w in range(x, total, 8))
-        assert mine == list(range(mine[0], mine[0] + len(mine))) if mine else True
+    whole = total // 256 * 256
+    for w in range(total):
+        x, i = w % 8, w // 8
+        if w < whole:
+            # XCD x (workgroups w = x mod 8) gets chunk x of each round of 8 chunks of 32.
+            assert out[w] // 32 % 8 == x and out[w] // 256 == i // 32
+        else:
+            assert out[w] == w
