@@ -34,6 +34,7 @@ BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 
 F32_PEAK_TFLOPS = 157.3      # MI355X dense fp32 matrix
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 KERNEL_SOURCES = ["newton_schulz_02_amd/csrc/kernels_gemm.hip",
+                  "newton_schulz_02_amd/csrc/tile_order.h",
                   "newton_schulz_02_amd/csrc/muon_internal.h"]
 
 
