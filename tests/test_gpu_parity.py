@@ -107,6 +107,51 @@ def test_layer4096_full_size():
         assert momentum_ok(res["M0"][i], res["G"][i], res["M1"][i], wl.beta, spec.dtype), spec.name
 
 
+def test_owner_share_full_size():
+    """One owner's 28 matrices and its packed AdamW tail at their real sizes, launched as the
+    bench launches them: one muon_step over all 28, then adamw_step on the same stream.
+
+    Momentum is checked for all 28 matrices; W' for the first square, the first wide and the
+    first tall matrix (each bucket); the tail in full against the oracle's AdamW step."""
+    wl = W.WORKLOADS["owner_share_32x4096_bf16"]
+    t = wl.tail
+    log(f"case {wl.name}: {wl.count} matrices + {t.numel} tail values")
+    items = list(W.generate(wl, weights="zeros"))
+    specs = [s for s, _, _, _ in items]
+    params = [w.to(DEV) for _, w, _, _ in items]
+    grads = [g.to(DEV) for _, _, g, _ in items]
+    moms = [m.to(DEV) for _, _, _, m in items]
+    tp, tg, tm, tv = W.generate_tail(wl)
+    dp, dg, dm, dv = (x.to(DEV) for x in (tp, tg, tm, tv))
+    stream = torch.cuda.current_stream()
+    step = nm.MuonStep(params, grads, moms, lr=wl.lr, beta=wl.beta, coeffs=wl.coeffs,
+                       steps=wl.steps, eps=wl.eps)
+    step(stream)
+    nm.adamw_step(dp, dg, dm, dv, lr=t.lr, beta1=t.beta1, beta2=t.beta2, eps=t.eps,
+                  weight_decay=t.weight_decay, step=t.step, stream=stream)
+    torch.cuda.synchronize()
+    res = {"specs": specs, "W0": [w for _, w, _, _ in items], "G": [g for _, _, g, _ in items],
+           "M0": [m for _, _, _, m in items], "W1": [p.cpu() for p in params],
+           "M1": [m.cpu() for m in moms]}
+    del params, grads, moms
+    for i, spec in enumerate(specs):
+        assert momentum_ok(res["M0"][i], res["G"][i], res["M1"][i], wl.beta, spec.dtype), spec.name
+    picks = {}
+    for i, spec in enumerate(specs):
+        kind = "square" if spec.rows == spec.cols else ("wide" if spec.rows < spec.cols else "tall")
+        picks.setdefault(kind, i)
+    assert sorted(picks) == ["square", "tall", "wide"]
+    for i in picks.values():
+        check_matrix(res, i, wl)
+    p0, g0, m0, v0 = to64(tp), to64(tg), to64(tm), to64(tv)
+    pr, mr, vr = oracle_adamw(p0, g0, m0, v0, t=t.step, lr=t.lr, beta1=t.beta1, beta2=t.beta2,
+                              eps=t.eps, weight_decay=t.weight_decay)
+    bp, bm, bv = adamw_bounds(p0, g0, m0, v0, t.step, t)
+    assert np.all(np.abs(to64(dm) - mr) <= bm)
+    assert np.all(np.abs(to64(dv) - vr) <= bv)
+    assert np.all(np.abs(to64(dp) - pr) <= bp)
+
+
 def test_many_small_one_per_bucket():
     wl = W.WORKLOADS["many_small_512_bf16"]
     log(f"case {wl.name}")
