@@ -122,6 +122,25 @@ int adamw_step(float* p, const float* g, float* m, float* v, int64_t n, const ad
 int muon_step_cost(const muon_matrix* mats, int32_t count, const muon_hparams* hp,
                    double* flops, double* bytes);
 
+/* Owner assignment (DMuon summary §2.3: each matrix gets one owner rank; the assignment
+ * minimises the predicted makespan, the largest total cost of one owner; the summary poses
+ * it as a mixed-integer program with a greedy fallback for large instances).  Host only.
+ *   cost[i]    predicted cost of matrix i (e.g. its measured step time), finite, >= 0;
+ *   count      number of matrices (>= 0), ranks the number of owners (>= 1);
+ *   node_limit budget of the exact search (0: greedy only);
+ *   owner[i]   receives the owner, in [0, ranks), of matrix i (count ints, caller-owned);
+ *   *makespan  receives the largest owner load (may be NULL);
+ *   *optimal   receives 1 when the result is proven optimal, else 0 (may be NULL).
+ * Greedy longest-first: matrices in decreasing cost (ties in list order), each to the owner
+ * with the smallest load so far (lowest index on ties).  Then, for count <= 64 and
+ * node_limit > 0, an exact depth-first search from the greedy makespan.  It returns the
+ * optimum when it finishes within node_limit nodes, else the best assignment found.  A
+ * result is also proven optimal when it meets max(largest cost, total / ranks).  Errors:
+ * MUON_EINVAL for bad sizes, NULL arrays or a negative or non-finite cost; nothing is
+ * written then. */
+int muon_owner_assign(const double* cost, int32_t count, int32_t ranks, int64_t node_limit,
+                      int32_t* owner, double* makespan, int32_t* optimal);
+
 /* Host-side description of the launch plan (buckets, restart sets, launches) as a
  * NUL-terminated JSON string written to buf (truncated to len).  Host only.  For tests. */
 int muon_plan_describe(const muon_matrix* mats, int32_t count, const muon_hparams* hp, char* buf,

@@ -81,6 +81,8 @@ _SIGNATURES = {
     "muon_shutdown": (None, []),
     "muon_debug_tile_order": (c_int, [c_int, c_int, c_int, POINTER(c_int), POINTER(c_int)]),
     "muon_debug_xcd_remap": (c_int, [c_int, POINTER(c_int)]),
+    "muon_owner_assign": (c_int, [POINTER(c_double), c_int32, c_int32, c_int64, POINTER(c_int32),
+                                  POINTER(c_double), POINTER(c_int32)]),
 }
 
 _lib = None
@@ -201,6 +203,20 @@ def step_cost(arr, count: int, hp: muon_hparams) -> tuple[float, float]:
     f, b = c_double(0), c_double(0)
     _check(lib().muon_step_cost(arr, int(count), ctypes.byref(hp), ctypes.byref(f), ctypes.byref(b)))
     return f.value, b.value
+
+
+def owner_assign(costs, ranks: int, node_limit: int = 1_000_000):
+    """Owners for matrices of the given costs (``muon_owner_assign``).
+
+    Returns (owner list, makespan, optimal); optimal is True when the library proved the
+    makespan minimal."""
+    n = len(costs)
+    arr = (c_double * max(n, 1))(*[float(c) for c in costs])
+    out = (c_int32 * max(n, 1))()
+    mk, opt = c_double(0.0), c_int32(0)
+    _check(lib().muon_owner_assign(arr, n, int(ranks), int(node_limit), out, ctypes.byref(mk),
+                                   ctypes.byref(opt)))
+    return list(out[:n]), mk.value, bool(opt.value)
 
 
 def plan_describe(arr, count: int, hp: muon_hparams, size: int = 1 << 24) -> dict:
