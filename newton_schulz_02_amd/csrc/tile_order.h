@@ -24,13 +24,22 @@ constexpr int kXcds = 8;
 constexpr int kXcdChunk = 32;
 constexpr int kBand = 4;
 
-// Logical tile index of workgroup w in a grid of `total` workgroups.  Workgroups past the
-// last whole round of kXcds chunks keep their own index.
+// Logical tile index of workgroup w in a grid of `total` workgroups.  The workgroups past the
+// last whole round of kXcds chunks (all of them in a launch of fewer than kXcds * kXcdChunk
+// tiles) split the remaining tiles into one contiguous block per XCD, so they keep their L2
+// locality too.
 MUON_HD int xcd_remap(int w, int total) {
   const int round = kXcds * kXcdChunk;
-  if (w >= total / round * round) return w;
-  const int x = w % kXcds, i = w / kXcds;
-  return (i / kXcdChunk) * round + x * kXcdChunk + i % kXcdChunk;
+  const int whole = total / round * round;
+  if (w < whole) {
+    const int x = w % kXcds, i = w / kXcds;
+    return (i / kXcdChunk) * round + x * kXcdChunk + i % kXcdChunk;
+  }
+  // Tail: workgroups whole + j (j = 0 .. rest-1); XCD x gets q + (x < r) of them.
+  const int j = w - whole, rest = total - whole;
+  const int q = rest / kXcds, r = rest % kXcds;
+  const int x = j % kXcds, i = j / kXcds;
+  return whole + (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
 }
 
 // t in [0, T(T+1)/2) -> (ti, tj), ti >= tj, for a T x T tile grid.

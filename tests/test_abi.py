@@ -266,10 +266,21 @@ def test_xcd_remap_is_a_permutation_dealing_chunks_round_robin(total):
     out = nm.xcd_remap(total)
     assert sorted(out) == list(range(total))
     whole = total // 256 * 256
+    rest = total - whole
+    tail_of = {x: [] for x in range(8)}
     for w in range(total):
         x, i = w % 8, w // 8
         if w < whole:
             # XCD x (workgroups w = x mod 8) gets chunk x of each round of 8 chunks of 32.
             assert out[w] // 32 % 8 == x and out[w] // 256 == i // 32
         else:
-            assert out[w] == w
+            assert out[w] >= whole
+            tail_of[(w - whole) % 8].append(out[w])
+    # The tail: XCD x gets one contiguous block of ceil or floor(rest / 8) tiles, in order.
+    start = whole
+    for x in range(8):
+        blk = tail_of[x]
+        assert blk == list(range(start, start + len(blk)))
+        assert len(blk) in (rest // 8, -(-rest // 8))
+        start += len(blk)
+    assert start == total
