@@ -33,31 +33,34 @@ METRIC = "Muon NS step TFLOP/s + matrices/s, % of bf16 MFMA peak (1 GPU)"
 BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 flop/clk/CU
 F32_PEAK_TFLOPS = 157.3      # MI355X dense fp32 matrix
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
-KERNEL_SOURCES = ["newton_schulz_02_amd/csrc/kernels_gemm.hip",
-                  "newton_schulz_02_amd/csrc/tile_order.h",
-                  "newton_schulz_02_amd/csrc/muon_internal.h"]
+_COMMON = ["newton_schulz_02_amd/csrc/tile_order.h", "newton_schulz_02_amd/csrc/muon_internal.h"]
+KERNEL_SOURCES = {  # sources each MFMA kernel is built from
+    "gemm": ["newton_schulz_02_amd/csrc/kernels_gemm.hip"] + _COMMON,
+    "gemm_wide": ["newton_schulz_02_amd/csrc/kernels_gemm_wide.hip"] + _COMMON,
+}
 
 
-def kernel_hash() -> str:
+def kernel_hash(kernel: str = "gemm_bf16") -> str:
+    """Hash of the sources of an MFMA kernel ("gemm_bf16", "gemm_wide_bf16", ...)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel.rsplit("_", 1)[0]]:
         h.update((ROOT / rel).read_bytes())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str):
-    """HBM bytes per launch of the contraction kernel from the committed counter summary.
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch of an MFMA kernel from the committed counter summary.
 
     The summary records the kernel source hash it was taken with; a different hash means
     the kernel changed since, and the figure is withheld (None).
     """
-    path = ROOT / "profiles" / f"gemm_bf16_{workload}_hbm_traffic.md"
+    path = ROOT / "profiles" / f"{kernel}_{workload}_hbm_traffic.md"
     if not path.exists():
         return None
     text = path.read_text()
     m_hash = re.search(r"kernel_hash:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash():
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash(kernel):
         return None
     return float(m_bytes.group(1))
 
@@ -132,6 +135,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--kernel", choices=["tuned", "square", "wide"], default="tuned",
+                    help="MFMA kernel per launch: measured at set-up (tuned) or one fixed")
+    ap.add_argument("--tune-reps", type=int, default=3)
+    ap.add_argument("--tune-cache", default="", metavar="FILE",
+                    help="tuning table to load before set-up (if it exists) and save after")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -168,6 +176,24 @@ def main() -> int:
             nm.adamw_step(*tail, lr=t.lr, beta1=t.beta1, beta2=t.beta2, eps=t.eps,
                           weight_decay=t.weight_decay, step=t.step, stream=stream)
 
+    # Set-up, untimed: pick the MFMA kernel configuration of each launch.
+    t0 = time.perf_counter()
+    nm.tune_force({"tuned": None, "square": nm.CFG_SQUARE, "wide": nm.CFG_WIDE}[args.kernel])
+    cache = Path(args.tune_cache) if args.tune_cache else None
+    if args.kernel == "tuned":
+        if cache and cache.exists():
+            nm.tune_import(cache.read_text())
+        table = nm.tune_table()
+        plan = nm.plan_describe(step.arr, step.count, step.hp)
+        if any(L["signature"] not in table for L in plan["launches"] if L["kind"] == "gemm"):
+            step.tune(stream, reps=args.tune_reps)
+        if cache:
+            cache.write_text(nm.tune_export())
+    plan = nm.plan_describe(step.arr, step.count, step.hp)
+    cfg_of_launch = [L["cfg"] for L in plan["launches"] if L["kind"] == "gemm"]
+    print(f"[bench] kernel per MFMA launch ({args.kernel}, {time.perf_counter() - t0:.1f} s): "
+          f"{cfg_of_launch}", file=sys.stderr, flush=True)
+
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
@@ -187,13 +213,14 @@ def main() -> int:
     ms = start.elapsed_time(stop) / args.steps
 
     value = flops / (ms * 1e-3) / 1e12
-    gemm_name = "gemm_bf16" if "gemm_bf16" in stats else "gemm_f32"
+    # The dominant MFMA kernel: the one with the most time in the timed steps.
+    gemm_name = max((k for k in stats if k.startswith("gemm")), key=lambda k: stats[k]["ms"])
     gs = stats[gemm_name]
-    peak = BF16_PEAK_TFLOPS if gemm_name == "gemm_bf16" else F32_PEAK_TFLOPS
+    peak = BF16_PEAK_TFLOPS if gemm_name.endswith("bf16") else F32_PEAK_TFLOPS
     avg_ms = gs["ms"] / gs["launches"]
     flops_per_launch = gs["flops"] / gs["launches"]
     achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
-    traffic = traffic_from_profiles(wl.name)
+    traffic = traffic_from_profiles(gemm_name, wl.name)
     kernels = {k: {"launches": v["launches"] // args.steps, "ms_per_step": v["ms"] / args.steps,
                    "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None,
                    "gbs": (v["bytes"] / (v["ms"] * 1e-3) / 1e9) if v["bytes"] else None}
@@ -229,6 +256,8 @@ def main() -> int:
             "ns_steps": wl.steps,
             "coeffs": list(wl.coeffs),
             "adamw_tail": wl.tail.numel if wl.tail else 0,
+            "kernel_selection": args.kernel,
+            "mfma_kernel_per_launch": ["256x384" if c else "256x256" for c in cfg_of_launch],
         },
         "roofline": {
             "bound": "mfma",

@@ -141,6 +141,38 @@ int muon_step_cost(const muon_matrix* mats, int32_t count, const muon_hparams* h
 int muon_owner_assign(const double* cost, int32_t count, int32_t ranks, int64_t node_limit,
                       int32_t* owner, double* makespan, int32_t* optimal);
 
+/* Shape-adaptive kernel selection (DMuon summary §2.4: the tile shape is searched per
+ * target and matrix shape, and the best configuration is cached and reused by later steps).
+ * The library has two MFMA kernel configurations: 0 = 256 x 256 output tiles, 1 = 256 x 384
+ * output tiles (8 waves of 128 x 96).  Each MFMA launch of a plan has a signature string
+ * (dtype, then per shape group its kind, symmetry, orientation and run-length shapes); a
+ * process-wide table maps signatures to configurations, and muon_step uses configuration 0
+ * for a signature the table does not hold.  The table is shared by all threads and devices.
+ * Configuration 1 addresses operands with 32-bit offsets: a launch holding a matrix whose
+ * larger side d has (d + 384) * (d rounded up to 128) * element size >= 2^31 bytes always
+ * runs configuration 0, whatever the table or muon_tune_force say.
+ *
+ * muon_tune: runs one step over device copies of the list's params and momenta (the
+ *   caller's matrices are not modified), and after each MFMA launch of that step times the
+ *   same launch `reps` (>= 1) times under each configuration.  The fastest is stored under
+ *   the launch's signature.  A set-up call: it allocates the copies with hipMalloc, frees
+ *   them before returning and synchronises the stream.  Arguments and errors as muon_step,
+ *   plus MUON_EINVAL for reps < 1 and MUON_EHIP when the copies cannot be allocated.
+ * muon_tune_force: cfg in {0, 1} forces that configuration for every launch, -1 restores
+ *   the table.  MUON_EINVAL for other values.  For tests and measurements.
+ * muon_tune_clear: empties the table.
+ * muon_tune_export: writes the table as text, one "signature cfg" line per entry, sorted,
+ *   NUL-terminated, into buf (len bytes).  *needed (may be NULL) receives the size with the
+ *   NUL; buf == NULL only queries it.  MUON_ENOSPC when len is too small (buf untouched).
+ * muon_tune_import: adds the lines of such a text to the table (existing signatures are
+ *   overwritten).  MUON_EINVAL, with nothing added, on a malformed line.  Host only. */
+int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, void* workspace,
+              size_t workspace_bytes, void* hip_stream, int32_t reps);
+int muon_tune_force(int32_t cfg);
+void muon_tune_clear(void);
+int muon_tune_export(char* buf, size_t len, size_t* needed);
+int muon_tune_import(const char* text);
+
 /* Host-side description of the launch plan (buckets, restart sets, launches) as a
  * NUL-terminated JSON string written to buf (truncated to len).  Host only.  For tests. */
 int muon_plan_describe(const muon_matrix* mats, int32_t count, const muon_hparams* hp, char* buf,
@@ -167,6 +199,10 @@ int muon_profile_end(muon_kernel_stat* out, int32_t max, int32_t* count);
  * muon_debug_xcd_remap: workgroup w -> logical tile out[w] for a grid of `total`. */
 int muon_debug_tile_order(int tri, int tm, int tn, int* ti, int* tj);
 int muon_debug_xcd_remap(int total, int* out);
+/* muon_debug_wide_tile_order: the same for the 256 x 384 configuration over a rows x cols
+ * output: tri != 0 walks the 256 x 384 tiles that meet the lower triangle of a rows x rows
+ * output (ti: 256-row band, tj: 384-column band).  Returns the tile count. */
+int muon_debug_wide_tile_order(int tri, int rows, int cols, int* ti, int* tj);
 
 const char* muon_strerror(int status); /* static string */
 const char* muon_last_error(void);     /* detail of the last failure on this thread */

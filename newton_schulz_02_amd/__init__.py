@@ -83,6 +83,12 @@ _SIGNATURES = {
     "muon_debug_xcd_remap": (c_int, [c_int, POINTER(c_int)]),
     "muon_owner_assign": (c_int, [POINTER(c_double), c_int32, c_int32, c_int64, POINTER(c_int32),
                                   POINTER(c_double), POINTER(c_int32)]),
+    "muon_tune": (c_int, [_MATP, c_int32, _HPP, c_void_p, c_size_t, c_void_p, c_int32]),
+    "muon_tune_force": (c_int, [c_int32]),
+    "muon_tune_clear": (None, []),
+    "muon_tune_export": (c_int, [c_char_p, c_size_t, POINTER(c_size_t)]),
+    "muon_tune_import": (c_int, [c_char_p]),
+    "muon_debug_wide_tile_order": (c_int, [c_int, c_int, c_int, POINTER(c_int), POINTER(c_int)]),
 }
 
 _lib = None
@@ -195,6 +201,41 @@ def step_raw(arr, count: int, hp: muon_hparams, ws_ptr: int, ws_bytes: int, stre
                            stream_ptr))
 
 
+def tune_raw(arr, count: int, hp: muon_hparams, ws_ptr: int, ws_bytes: int, stream_ptr,
+             reps: int = 3) -> None:
+    _check(lib().muon_tune(arr, int(count), ctypes.byref(hp), c_void_p(ws_ptr), int(ws_bytes),
+                           stream_ptr, int(reps)))
+
+
+CFG_SQUARE, CFG_WIDE = 0, 1  # MFMA kernel configurations: 256 x 256 and 256 x 384 tiles
+
+
+def tune_force(cfg) -> None:
+    """Force one kernel configuration for every launch (None: use the tuning table)."""
+    _check(lib().muon_tune_force(-1 if cfg is None else int(cfg)))
+
+
+def tune_clear() -> None:
+    lib().muon_tune_clear()
+
+
+def tune_export() -> str:
+    """The tuning table as text: one "signature cfg" line per entry."""
+    need = c_size_t(0)
+    _check(lib().muon_tune_export(None, 0, ctypes.byref(need)))
+    buf = ctypes.create_string_buffer(need.value)
+    _check(lib().muon_tune_export(buf, need.value, ctypes.byref(need)))
+    return buf.value.decode()
+
+
+def tune_import(text: str) -> None:
+    _check(lib().muon_tune_import(text.encode()))
+
+
+def tune_table() -> dict:
+    return {sig: int(c) for sig, c in (ln.rsplit(" ", 1) for ln in tune_export().splitlines() if ln)}
+
+
 def workspace_size(params, grads, moms, **hp) -> int:
     return workspace_size_raw(matrix_array(params, grads, moms), len(params), make_hparams(**hp))
 
@@ -255,6 +296,12 @@ class MuonStep:
         step_raw(self.arr, self.count, self.hp, self.workspace.data_ptr(), self.workspace.numel(),
                  _stream_handle(stream, self.device))
 
+    def tune(self, stream=None, reps: int = 3) -> None:
+        """Time every MFMA launch of this step under each kernel configuration and cache the
+        fastest (``muon_tune``); runs on copies, so params and momenta are unchanged."""
+        tune_raw(self.arr, self.count, self.hp, self.workspace.data_ptr(), self.workspace.numel(),
+                 _stream_handle(stream, self.device), reps)
+
 
 def muon_step(params, grads, moms, *, stream=None, **hp) -> None:
     """One Muon step over lists of device tensors (param and momentum updated in place)."""
@@ -282,6 +329,15 @@ def tile_order(tri: bool, tm: int, tn: int = 0):
     n = tm * (tm + 1) // 2 if tri else tm * tn
     ti, tj = (c_int * max(n, 1))(), (c_int * max(n, 1))()
     lib().muon_debug_tile_order(int(bool(tri)), tm, tn, ti, tj)
+    return list(zip(ti[:n], tj[:n]))
+
+
+def wide_tile_order(tri: bool, rows: int, cols: int = 0):
+    """Test hook: the (ti, tj) order of the 256 x 384 configuration over a rows x cols output
+    (tri: the tiles meeting the lower triangle of a rows x rows output)."""
+    n = lib().muon_debug_wide_tile_order(int(bool(tri)), rows, cols, None, None)
+    ti, tj = (c_int * max(n, 1))(), (c_int * max(n, 1))()
+    lib().muon_debug_wide_tile_order(int(bool(tri)), rows, cols, ti, tj)
     return list(zip(ti[:n], tj[:n]))
 
 

@@ -58,6 +58,18 @@ struct Rec {
 };
 bool g_prof = false;
 std::vector<Rec> g_recs;
+
+// Kernel configuration per launch signature (filled by muon_tune or muon_tune_import), and
+// a forced configuration for every launch (-1: none).
+std::map<std::string, int> g_tune;
+int g_force_cfg = -1;
+
+// Caller holds g_mu.
+int choose_cfg(const std::string& sig) {
+  if (g_force_cfg >= 0) return g_force_cfg;
+  auto it = g_tune.find(sig);
+  return it == g_tune.end() ? int(kCfgSquare) : it->second;
+}
 std::map<int, std::vector<hipEvent_t>> g_event_pool;
 
 int current_device(int* dev) {
@@ -148,6 +160,74 @@ int timed(int dev, hipStream_t s, const char* name, double flops, double bytes, 
   return MUON_OK;
 }
 
+// Enqueue one launch of the plan on stream s.  Caller holds g_mu.
+int run_launch(int dev, hipStream_t s, const Plan& plan, const PlanLaunch& L, int cfg, const MatDesc* ddesc,
+               float* scale, float* partials, const muon_hparams* hp, int count) {
+  if (L.kind == kLaunchMomentum) {
+    MomArgs a;
+    a.desc = ddesc;
+    a.partials = partials;
+    a.first = L.first;
+    a.last = L.last;
+    a.tile_begin = int32_t(plan.mats[L.first].mom_prefix);
+    a.total_tiles = int32_t(L.tiles);
+    a.beta = hp->beta;
+    return timed(dev, s, L.dtype == kBF16 ? "momentum_bf16" : "momentum_f32", 0.0, L.bytes,
+                 [&] { return muon_launch_momentum(a, L.dtype, s); });
+  }
+  if (L.kind == kLaunchNorm) {
+    NormArgs a;
+    a.desc = ddesc;
+    a.partials = partials;
+    a.scale = scale;
+    a.count = count;
+    a.eps = hp->eps;
+    return timed(dev, s, "norm", 0.0, 0.0, [&] { return muon_launch_norm(a, s); });
+  }
+  GemmArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.desc = ddesc;
+  a.scale = scale;
+  a.pa = hp->ns_a;
+  a.pb = hp->ns_b;
+  a.pc = hp->ns_c;
+  const std::vector<GroupArg>& groups = L.groups_cfg[cfg];
+  a.ngroups = int32_t(groups.size());
+  a.total_tiles = int32_t(L.tiles_cfg[cfg]);
+  for (size_t g = 0; g < groups.size(); ++g) a.g[g] = groups[g];
+  const bool bf = L.dtype == kBF16;
+  if (cfg == kCfgWide)
+    return timed(dev, s, bf ? "gemm_wide_bf16" : "gemm_wide_f32", L.flops, 0.0,
+                 [&] { return muon_launch_gemm_wide(a, L.dtype, s); });
+  return timed(dev, s, bf ? "gemm_bf16" : "gemm_f32", L.flops, 0.0,
+               [&] { return muon_launch_gemm(a, L.dtype, s); });
+}
+
+// Validate, plan (with the tuned kernel choices) and upload the descriptors.  Caller holds
+// g_mu.
+int prepare(const muon_matrix* mats, int32_t count, const muon_hparams* hp, void* workspace,
+            size_t workspace_bytes, hipStream_t s, Plan* plan, int* dev) {
+  std::string err;
+  const CfgChooser chooser = [](const std::string& sig) { return choose_cfg(sig); };
+  int rc = build_plan(mats, count, hp, plan, &err, &chooser);
+  if (rc != MUON_OK) return fail(rc, err);
+  if (count == 0) return MUON_OK;
+  if (!workspace) return fail(MUON_EINVAL, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(MUON_EINVAL, "workspace is not 256-byte aligned");
+  if (workspace_bytes < plan->ws_bytes) {
+    char buf[128];
+    snprintf(buf, sizeof buf, "workspace has %zu bytes, needs %zu", workspace_bytes, plan->ws_bytes);
+    return fail(MUON_ENOSPC, buf);
+  }
+  char* ws = static_cast<char*>(workspace);
+  std::vector<MatDesc> descs;
+  fill_descs(*plan, mats, hp, ws, &descs);
+  if ((rc = current_device(dev)) != MUON_OK) return rc;
+  if ((rc = check_device(*dev)) != MUON_OK) return rc;
+  return upload(*dev, descs.data(), descs.size() * sizeof(MatDesc), ws + plan->desc_off, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -204,7 +284,9 @@ int muon_plan_describe(const muon_matrix* mats, int32_t count, const muon_hparam
     if (!buf || len == 0) return fail(MUON_EINVAL, "buf is NULL or empty");
     Plan plan;
     std::string err;
-    const int rc = build_plan(mats, count, hp, &plan, &err);
+    std::lock_guard<std::mutex> lock(g_mu);
+    const CfgChooser chooser = [](const std::string& sig) { return choose_cfg(sig); };
+    const int rc = build_plan(mats, count, hp, &plan, &err, &chooser);
     if (rc != MUON_OK) return fail(rc, err);
     const std::string s = describe_plan(plan);
     const size_t n = std::min(len - 1, s.size());
@@ -220,76 +302,169 @@ int muon_plan_describe(const muon_matrix* mats, int32_t count, const muon_hparam
 int muon_step(const muon_matrix* mats, int32_t count, const muon_hparams* hp, void* workspace,
               size_t workspace_bytes, void* hip_stream) {
   try {
-    Plan plan;
-    std::string err;
-    int rc = build_plan(mats, count, hp, &plan, &err);
-    if (rc != MUON_OK) return fail(rc, err);
-    if (count == 0) return MUON_OK;
-    if (!workspace) return fail(MUON_EINVAL, "workspace is NULL");
-    if (reinterpret_cast<uintptr_t>(workspace) % 256)
-      return fail(MUON_EINVAL, "workspace is not 256-byte aligned");
-    if (workspace_bytes < plan.ws_bytes) {
-      char buf[128];
-      snprintf(buf, sizeof buf, "workspace has %zu bytes, needs %zu", workspace_bytes,
-               plan.ws_bytes);
-      return fail(MUON_ENOSPC, buf);
-    }
-    char* ws = static_cast<char*>(workspace);
-    std::vector<MatDesc> descs;
-    fill_descs(plan, mats, hp, ws, &descs);
-
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     std::lock_guard<std::mutex> lock(g_mu);
+    Plan plan;
     int dev = 0;
-    if ((rc = current_device(&dev)) != MUON_OK) return rc;
-    if ((rc = check_device(dev)) != MUON_OK) return rc;
-    if ((rc = upload(dev, descs.data(), descs.size() * sizeof(MatDesc), ws + plan.desc_off, s)) !=
-        MUON_OK)
-      return rc;
-
+    int rc = prepare(mats, count, hp, workspace, workspace_bytes, s, &plan, &dev);
+    if (rc != MUON_OK || count == 0) return rc;
+    char* ws = static_cast<char*>(workspace);
     const MatDesc* ddesc = reinterpret_cast<const MatDesc*>(ws + plan.desc_off);
     float* scale = reinterpret_cast<float*>(ws + plan.scale_off);
     float* partials = reinterpret_cast<float*>(ws + plan.partial_off);
     for (const PlanLaunch& L : plan.launches) {
-      if (L.kind == kLaunchMomentum) {
-        MomArgs a;
-        a.desc = ddesc;
-        a.partials = partials;
-        a.first = L.first;
-        a.last = L.last;
-        a.tile_begin = int32_t(plan.mats[L.first].mom_prefix);
-        a.total_tiles = int32_t(L.tiles);
-        a.beta = hp->beta;
-        rc = timed(dev, s, L.dtype == kBF16 ? "momentum_bf16" : "momentum_f32", 0.0, L.bytes,
-                   [&] { return muon_launch_momentum(a, L.dtype, s); });
-      } else if (L.kind == kLaunchNorm) {
-        NormArgs a;
-        a.desc = ddesc;
-        a.partials = partials;
-        a.scale = scale;
-        a.count = count;
-        a.eps = hp->eps;
-        rc = timed(dev, s, "norm", 0.0, 0.0, [&] { return muon_launch_norm(a, s); });
-      } else {
-        GemmArgs a;
-        std::memset(&a, 0, sizeof a);
-        a.desc = ddesc;
-        a.scale = scale;
-        a.pa = hp->ns_a;
-        a.pb = hp->ns_b;
-        a.pc = hp->ns_c;
-        a.ngroups = int32_t(L.groups.size());
-        a.total_tiles = int32_t(L.tiles);
-        for (size_t g = 0; g < L.groups.size(); ++g) a.g[g] = L.groups[g];
-        rc = timed(dev, s, L.dtype == kBF16 ? "gemm_bf16" : "gemm_f32", L.flops, 0.0,
-                   [&] { return muon_launch_gemm(a, L.dtype, s); });
-      }
+      rc = run_launch(dev, s, plan, L, L.cfg, ddesc, scale, partials, hp, count);
       if (rc != MUON_OK) return rc;
     }
     return MUON_OK;
   } catch (const std::exception& e) {
     return fail(MUON_EHIP, std::string("exception: ") + e.what());
   }
+}
+
+int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, void* workspace,
+              size_t workspace_bytes, void* hip_stream, int32_t reps) {
+  try {
+    if (reps < 1) return fail(MUON_EINVAL, "reps must be >= 1");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    std::lock_guard<std::mutex> lock(g_mu);
+    {  // validate the caller's list as muon_step would (host only)
+      Plan check;
+      std::string err;
+      const int rc = build_plan(mats, count, hp, &check, &err);
+      if (rc != MUON_OK) return fail(rc, err);
+      if (count == 0) return MUON_OK;
+    }
+    // The trial launches re-run in-place phases (momentum, the weight update), so the step
+    // runs on device copies of the params and momenta; the caller's matrices are unchanged.
+    std::vector<muon_matrix> shadow(mats, mats + count);
+    std::vector<size_t> off(size_t(count) * 2);
+    size_t total = 0;
+    for (int32_t i = 0; i < count; ++i) {
+      const size_t bytes = size_t(mats[i].rows) * size_t(mats[i].cols) * (mats[i].dtype == MUON_BF16 ? 2 : 4);
+      for (int k = 0; k < 2; ++k) {
+        off[size_t(i) * 2 + k] = total;
+        total += (bytes + 255) / 256 * 256;
+      }
+    }
+    char* copy = nullptr;
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&copy), total);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc (tuning copies)");
+    struct Free {
+      char* p;
+      ~Free() { hipFree(p); }
+    } release{copy};
+    for (int32_t i = 0; i < count && e == hipSuccess; ++i) {
+      const size_t bytes = size_t(mats[i].rows) * size_t(mats[i].cols) * (mats[i].dtype == MUON_BF16 ? 2 : 4);
+      shadow[size_t(i)].param = copy + off[size_t(i) * 2];
+      shadow[size_t(i)].momentum = copy + off[size_t(i) * 2 + 1];
+      e = hipMemcpyAsync(shadow[size_t(i)].param, mats[i].param, bytes, hipMemcpyDeviceToDevice, s);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(shadow[size_t(i)].momentum, mats[i].momentum, bytes, hipMemcpyDeviceToDevice, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (tuning copies)");
+
+    const int saved_force = g_force_cfg;
+    g_force_cfg = kCfgSquare;  // the plan's own groups are the square ones; trials use both
+    Plan plan;
+    int dev = 0;
+    int rc = prepare(shadow.data(), count, hp, workspace, workspace_bytes, s, &plan, &dev);
+    g_force_cfg = saved_force;
+    if (rc != MUON_OK) {
+      hipStreamSynchronize(s);
+      return rc;
+    }
+    char* ws = static_cast<char*>(workspace);
+    const MatDesc* ddesc = reinterpret_cast<const MatDesc*>(ws + plan.desc_off);
+    float* scale = reinterpret_cast<float*>(ws + plan.scale_off);
+    float* partials = reinterpret_cast<float*>(ws + plan.partial_off);
+    const bool prof = g_prof;
+    g_prof = false;  // the trial launches are not part of a profile
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    e = hipEventCreate(&ev[0]);
+    if (e == hipSuccess) e = hipEventCreate(&ev[1]);
+    // Every launch runs once in order, so that each sees the operands of a real step; then
+    // each MFMA launch is timed under every kernel configuration, reps launches each.  The
+    // kernels' run time does not depend on the values, so the trials' repeated in-place
+    // writes do not bias the later timings.
+    for (const PlanLaunch& L : plan.launches) {
+      if (e != hipSuccess || rc != MUON_OK) break;
+      rc = run_launch(dev, s, plan, L, kCfgSquare, ddesc, scale, partials, hp, count);
+      if (rc != MUON_OK || L.kind != kLaunchGemm) continue;
+      float best = 0.0f;
+      int best_cfg = kCfgSquare;
+      for (int cfg = 0; cfg < kNumCfg && rc == MUON_OK && e == hipSuccess; ++cfg) {
+        if (cfg == kCfgWide && !L.wide_ok) continue;
+        e = hipEventRecord(ev[0], s);
+        for (int r = 0; r < reps && rc == MUON_OK && e == hipSuccess; ++r)
+          rc = run_launch(dev, s, plan, L, cfg, ddesc, scale, partials, hp, count);
+        if (e == hipSuccess) e = hipEventRecord(ev[1], s);
+        if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+        if (e == hipSuccess && rc == MUON_OK && (cfg == kCfgSquare || ms < best)) {
+          best = ms;
+          best_cfg = cfg;
+        }
+      }
+      if (e == hipSuccess && rc == MUON_OK) g_tune[L.signature] = best_cfg;
+    }
+    g_prof = prof;
+    const hipError_t es = hipStreamSynchronize(s);  // before the copies are freed
+    for (hipEvent_t x : ev)
+      if (x) hipEventDestroy(x);
+    if (rc != MUON_OK) return rc;
+    if (e != hipSuccess) return hip_fail(e, "muon_tune timing");
+    if (es != hipSuccess) return hip_fail(es, "hipStreamSynchronize (tuning)");
+    return MUON_OK;
+  } catch (const std::exception& ex) {
+    return fail(MUON_EHIP, std::string("exception: ") + ex.what());
+  }
+}
+
+int muon_tune_force(int32_t cfg) {
+  if (cfg < -1 || cfg >= kNumCfg) return fail(MUON_EINVAL, "cfg must be -1, 0 or 1");
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_force_cfg = cfg;
+  return MUON_OK;
+}
+
+void muon_tune_clear(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_tune.clear();
+}
+
+int muon_tune_export(char* buf, size_t len, size_t* needed) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  std::string out;
+  for (const auto& kv : g_tune) out += kv.first + " " + std::to_string(kv.second) + "\n";
+  if (needed) *needed = out.size() + 1;
+  if (!buf) return MUON_OK;
+  if (len < out.size() + 1) return fail(MUON_ENOSPC, "buffer too small for the tuning table");
+  std::memcpy(buf, out.c_str(), out.size() + 1);
+  return MUON_OK;
+}
+
+int muon_tune_import(const char* text) {
+  if (!text) return fail(MUON_EINVAL, "text is NULL");
+  std::map<std::string, int> add;
+  const char* p = text;
+  while (*p) {
+    const char* eol = std::strchr(p, '\n');
+    const std::string line(p, eol ? size_t(eol - p) : std::strlen(p));
+    p = eol ? eol + 1 : p + line.size();
+    if (line.empty()) continue;
+    const size_t sp = line.rfind(' ');
+    if (sp == std::string::npos || sp == 0 || sp + 1 >= line.size())
+      return fail(MUON_EINVAL, "tuning line without 'signature cfg': " + line);
+    const std::string sig = line.substr(0, sp), val = line.substr(sp + 1);
+    if (sig.find(' ') != std::string::npos || (val != "0" && val != "1"))
+      return fail(MUON_EINVAL, "bad tuning line: " + line);
+    add[sig] = val == "1" ? kCfgWide : kCfgSquare;
+  }
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (const auto& kv : add) g_tune[kv.first] = kv.second;
+  return MUON_OK;
 }
 
 int adamw_step(float* p, const float* g, float* m, float* v, int64_t n, const adamw_hparams* hp,

@@ -15,7 +15,11 @@
 
 namespace muon {
 
-constexpr int kTile = 256;       // output tile edge of the MFMA kernels (both dtypes)
+constexpr int kTile = 256;       // output tile edge of the square-tile MFMA kernel
+constexpr int kWideM = 256;      // output tile rows of the wide-tile MFMA kernel
+constexpr int kWideN = 384;      // output tile columns of the wide-tile MFMA kernel
+// MFMA kernel configurations (chosen per launch: tuned, or the square one by default).
+enum GemmCfg : int32_t { kCfgSquare = 0, kCfgWide = 1, kNumCfg = 2 };
 constexpr int kKPad = 128;       // contraction dimensions are padded to this multiple
 constexpr int kEwTile = 64;      // tile edge of the momentum/transpose kernel
 constexpr int kMaxGroups = 8;    // op groups per grouped GEMM launch
@@ -71,12 +75,16 @@ struct MatDesc {
   int32_t tri_prefix;    // first lower-triangle GEMM tile (prefix over sorted order)
   int32_t full_prefix;   // first full GEMM tile (prefix over sorted order)
   float eta;             // lr * sqrt(max(1, rows/cols))
+  // The same prefixes for the wide-tile kernel: symmetric m x m outputs, full m x n
+  // outputs, full n x m outputs (the update of a tall matrix).
+  int32_t wide_prefix[3];
 };
 
 struct GroupArg {
   int32_t first, last;   // matrix range [first, last) in the descriptor table
   int32_t tile_begin;    // first launch tile of this group
   int8_t kind, a, b, c, c2, e, alpha, tri;
+  int8_t nm;             // full output of n x m elements (the update of a tall matrix)
 };
 
 struct GemmArgs {
@@ -124,4 +132,5 @@ inline int64_t ceil_div(int64_t x, int64_t q) { return (x + q - 1) / q; }
 int muon_launch_momentum(const muon::MomArgs& a, int dtype, void* stream);
 int muon_launch_norm(const muon::NormArgs& a, void* stream);
 int muon_launch_gemm(const muon::GemmArgs& a, int dtype, void* stream);
+int muon_launch_gemm_wide(const muon::GemmArgs& a, int dtype, void* stream);
 int muon_launch_adamw(const muon::AdamArgs& a, void* stream);

@@ -8,6 +8,7 @@
 // Matrices are sorted into shape buckets and same-level ops of a bucket share one launch
 // (DMuon summary §2.2, batching of similar shapes).
 #include "planner.h"
+#include "tile_order.h"
 
 #include <algorithm>
 #include <climits>
@@ -177,7 +178,7 @@ uint32_t resolve_restarts(uint32_t mask, int64_t m, int64_t n, int steps) {
 }
 
 int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, Plan* plan,
-               std::string* err) {
+               std::string* err, const CfgChooser* choose) {
   *plan = Plan();
   if (count < 0) {
     *err = "count is negative";
@@ -295,7 +296,7 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
 
   // Schedules and tile counts.
   int max_level = -1;
-  int64_t tri = 0, full = 0, mom = 0;
+  int64_t tri = 0, full = 0, mom = 0, wide[3] = {0, 0, 0};
   for (PlanMat& p : plan->mats) {
     std::vector<SOp> sops;
     const int nv = schedule(steps, p.restarts, p.tall, &sops);
@@ -309,6 +310,13 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
     }
     p.tri_tiles = tri_tiles_of(p.m);
     p.full_tiles = full_tiles_of(p.m, p.n);
+    p.wide_tiles[0] = sym_tiles(int(p.m), kWideM, kWideN);
+    p.wide_tiles[1] = ceil_div(p.m, kWideM) * ceil_div(p.n, kWideN);
+    p.wide_tiles[2] = ceil_div(p.n, kWideM) * ceil_div(p.m, kWideN);
+    {  // largest operand, with a tile's overhang of rows, below 2^31 bytes
+      const int64_t big = std::max(p.m, p.n);
+      p.wide_ok = (big + kWideN) * round_up(big, kKPad) * int64_t(p.esize) < (int64_t(1) << 31);
+    }
     // Momentum tiles cover the extents rounded up to kKPad, so that the zero padding of the
     // row and transposed copies (leading dimensions rounded to kKPad) is written too.
     p.mom_tiles_c = round_up(p.c, kKPad) / kEwTile;
@@ -316,6 +324,10 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
     p.mom_tiles = p.mom_tiles_r * p.mom_tiles_c;
     p.tri_prefix = tri;
     p.full_prefix = full;
+    for (int k = 0; k < 3; ++k) {
+      p.wide_prefix[k] = wide[k];
+      wide[k] += p.wide_tiles[k];
+    }
     p.mom_prefix = mom;
     tri += p.tri_tiles;
     full += p.full_tiles;
@@ -325,7 +337,8 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
     plan->flops += p.flops;
     plan->bytes += p.bytes;
   }
-  if (tri > INT32_MAX || full > INT32_MAX || mom > INT32_MAX) {
+  if (tri > INT32_MAX || full > INT32_MAX || mom > INT32_MAX || wide[0] > INT32_MAX ||
+      wide[1] > INT32_MAX || wide[2] > INT32_MAX) {
     *err = "too many tiles for one call";
     return MUON_EINVAL;
   }
@@ -425,13 +438,14 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
         L.kind = kLaunchGemm;
         L.dtype = plan->mats[f].dtype;
         L.level = lev;
-        int64_t tiles = 0;
+        std::ostringstream sig;
+        sig << (L.dtype == kBF16 ? "bf16" : "f32");
         for (size_t gi = g0; gi < std::min(groups.size(), g0 + kMaxGroups); ++gi) {
           const G& g = groups[gi];
+          const PlanMat& p0 = plan->mats[g.first];
           GroupArg a;
           a.first = g.first;
           a.last = g.last;
-          a.tile_begin = int32_t(tiles);
           a.kind = g.op.kind;
           a.a = g.op.a;
           a.b = g.op.b;
@@ -440,18 +454,37 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
           a.e = g.op.e;
           a.alpha = g.op.alpha;
           a.tri = g.op.tri;
-          for (int i = g.first; i < g.last; ++i) {
-            const PlanMat& p = plan->mats[i];
-            tiles += g.op.tri ? p.tri_tiles : p.full_tiles;
-            L.flops += op_flops(g.op, p.m, p.n);
+          a.nm = (g.op.kind == kOpUpdate && p0.tall) ? 1 : 0;  // W is n x m
+          for (int i = g.first; i < g.last; ++i) L.wide_ok = L.wide_ok && plan->mats[i].wide_ok;
+          for (int cfg = 0; cfg < kNumCfg; ++cfg) {
+            a.tile_begin = int32_t(L.tiles_cfg[cfg]);
+            for (int i = g.first; i < g.last; ++i) {
+              const PlanMat& p = plan->mats[i];
+              if (cfg == kCfgSquare) L.tiles_cfg[cfg] += g.op.tri ? p.tri_tiles : p.full_tiles;
+              else L.tiles_cfg[cfg] += p.wide_tiles[g.op.tri ? 0 : (a.nm ? 2 : 1)];
+            }
+            L.groups_cfg[cfg].push_back(a);
           }
-          L.groups.push_back(a);
+          for (int i = g.first; i < g.last; ++i) L.flops += op_flops(g.op, plan->mats[i].m, plan->mats[i].n);
+          sig << "|" << int(g.op.kind) << ":" << int(g.op.tri) << ":" << int(a.nm);
+          for (int i = g.first; i < g.last;) {  // shapes of the group, run-length encoded
+            int j = i;
+            while (j < g.last && plan->mats[j].m == plan->mats[i].m && plan->mats[j].n == plan->mats[i].n) ++j;
+            sig << ":" << plan->mats[i].m << "x" << plan->mats[i].n << "*" << (j - i);
+            i = j;
+          }
         }
-        L.tiles = tiles;
-        if (tiles > INT32_MAX) {
-          *err = "too many tiles in one launch";
-          return MUON_EINVAL;
+        for (int cfg = 0; cfg < kNumCfg; ++cfg) {
+          if (L.tiles_cfg[cfg] > INT32_MAX) {
+            *err = "too many tiles in one launch";
+            return MUON_EINVAL;
+          }
         }
+        L.signature = sig.str();
+        L.cfg = choose ? (*choose)(L.signature) : kCfgSquare;
+        if (L.cfg < 0 || L.cfg >= kNumCfg || (L.cfg == kCfgWide && !L.wide_ok)) L.cfg = kCfgSquare;
+        L.groups = L.groups_cfg[L.cfg];
+        L.tiles = L.tiles_cfg[L.cfg];
         plan->launches.push_back(L);
       }
     }
@@ -519,6 +552,7 @@ void fill_descs(const Plan& plan, const muon_matrix* mats, const muon_hparams* h
     d.mom_tiles_r = int32_t(p.mom_tiles_r);
     d.tri_prefix = int32_t(p.tri_prefix);
     d.full_prefix = int32_t(p.full_prefix);
+    for (int k = 0; k < 3; ++k) d.wide_prefix[k] = int32_t(p.wide_prefix[k]);
     d.eta = float(double(hp->lr) * std::sqrt(std::max(1.0, double(p.r) / double(p.c))));
   }
 }
@@ -550,7 +584,10 @@ std::string describe_plan(const Plan& plan) {
   for (size_t i = 0; i < plan.launches.size(); ++i) {
     const PlanLaunch& L = plan.launches[i];
     os << (i ? "," : "") << "{\"kind\":\"" << kLaunch[L.kind] << "\",\"dtype\":" << L.dtype
-       << ",\"level\":" << L.level << ",\"tiles\":" << L.tiles << ",\"flops\":" << L.flops
+       << ",\"level\":" << L.level << ",\"tiles\":" << L.tiles << ",\"cfg\":" << L.cfg
+       << ",\"tiles_cfg\":[" << L.tiles_cfg[0] << "," << L.tiles_cfg[1] << "]"
+       << ",\"wide_ok\":" << (L.wide_ok ? "true" : "false")
+       << ",\"signature\":\"" << L.signature << "\",\"flops\":" << L.flops
        << ",\"groups\":[";
     for (size_t g = 0; g < L.groups.size(); ++g) {
       const GroupArg& a = L.groups[g];

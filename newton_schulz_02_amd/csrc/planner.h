@@ -3,6 +3,7 @@
 // the grouped launch list.  Pure C++: no HIP call, so it runs (and is tested) without a GPU.
 #pragma once
 
+#include <functional>
 #include <string>
 #include <vector>
 
@@ -33,6 +34,10 @@ struct PlanMat {
   int64_t trans_off = -1;        // reserved transposed copy
   int64_t tri_tiles = 0, full_tiles = 0, mom_tiles = 0, mom_tiles_c = 0, mom_tiles_r = 0;
   int64_t tri_prefix = 0, full_prefix = 0, mom_prefix = 0;
+  // Wide-tile kernel: tiles of a symmetric m x m, a full m x n and a full n x m output, and
+  // their prefixes over the sorted order.
+  int64_t wide_tiles[3] = {0, 0, 0}, wide_prefix[3] = {0, 0, 0};
+  bool wide_ok = true;  // every operand fits the 256 x 384 kernel's 32-bit buffer offsets
   double flops = 0, bytes = 0;
 };
 
@@ -43,8 +48,13 @@ struct PlanLaunch {
   int dtype = kBF16;
   int level = -1;
   int first = 0, last = 0;       // momentum: matrix range
-  std::vector<GroupArg> groups;  // gemm
+  std::vector<GroupArg> groups;  // gemm: the groups of the chosen kernel configuration
   int64_t tiles = 0;
+  int cfg = kCfgSquare;          // gemm: the chosen MFMA kernel configuration
+  std::vector<GroupArg> groups_cfg[kNumCfg];  // gemm: the groups under each configuration
+  int64_t tiles_cfg[kNumCfg] = {0, 0};
+  bool wide_ok = true;           // gemm: the 256 x 384 configuration may run this launch
+  std::string signature;         // gemm: shapes and ops of the launch (the tuning key)
   double flops = 0, bytes = 0;
 };
 
@@ -58,9 +68,14 @@ struct Plan {
   double flops = 0, bytes = 0;
 };
 
-// Validate and plan.  Returns MUON_OK or a negative muon_status with *err set.
+// Chooses the MFMA kernel configuration of a launch from its signature (kCfgSquare when
+// there is no entry).
+using CfgChooser = std::function<int(const std::string& signature)>;
+
+// Validate and plan.  Returns MUON_OK or a negative muon_status with *err set.  Without a
+// chooser every launch uses the square-tile kernel.
 int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, Plan* plan,
-               std::string* err);
+               std::string* err, const CfgChooser* choose = nullptr);
 
 // Fill the device descriptor table for a concrete workspace base address.
 void fill_descs(const Plan& plan, const muon_matrix* mats, const muon_hparams* hp, char* ws,

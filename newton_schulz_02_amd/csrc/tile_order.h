@@ -12,8 +12,8 @@
 //    triangle (ti >= tj), full_band_decode() over a full TM x TN grid.
 #pragma once
 
-#ifdef __HIPCC__
-#define MUON_HD __host__ __device__ __forceinline__
+#if defined(__HIP__)
+#define MUON_HD __attribute__((host)) __attribute__((device)) inline
 #else
 #define MUON_HD inline
 #endif
@@ -63,6 +63,59 @@ MUON_HD void tri_band_decode(int t, int T, int& ti, int& tj) {
     }
     tj = 4 * s + c;
     ti = 4 * s + c + v;
+  }
+}
+
+// ---- non-square tiles (TM rows x TN columns) ----------------------------------------
+// A symmetric m x m output is computed on the tiles that hold an element on or below the
+// diagonal (each such element lies in exactly one of them).
+
+MUON_HD int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
+
+// Column tiles of tile row ti that reach the diagonal (column tiles tj with TN tj <= the
+// tile row's last row); it never decreases with ti.
+MUON_HD int sym_row_tiles(int ti, int m, int TM, int TN) {
+  const int last_row = (TM * ti + TM - 1 < m - 1) ? TM * ti + TM - 1 : m - 1;
+  const int k = last_row / TN + 1;
+  const int tn = ceil_div_i(m, TN);
+  return k < tn ? k : tn;
+}
+
+// Number of tiles of a symmetric m x m output.
+MUON_HD int sym_tiles(int m, int TM, int TN) {
+  int n = 0;
+  const int tm = ceil_div_i(m, TM);
+  for (int ti = 0; ti < tm; ++ti) n += sym_row_tiles(ti, m, TM, TN);
+  return n;
+}
+
+// t in [0, sym_tiles(m, TM, TN)) -> (ti, tj).  Bands of kBand tile rows; inside a band,
+// column by column, the band rows whose tile row reaches that column (a suffix of the
+// band).  With TM == TN this is tri_band_decode's order.
+MUON_HD void sym_decode(int t, int m, int TM, int TN, int& ti, int& tj) {
+  const int tm = ceil_div_i(m, TM);
+  const int tn = ceil_div_i(m, TN);
+  int r0 = 0;
+  int h = tm < kBand ? tm : kBand;
+  for (;;) {
+    int cnt = 0;
+    for (int r = 0; r < h; ++r) cnt += sym_row_tiles(r0 + r, m, TM, TN);
+    if (t < cnt || r0 + h >= tm) break;
+    t -= cnt;
+    r0 += h;
+    h = tm - r0 < kBand ? tm - r0 : kBand;
+  }
+  ti = r0;
+  tj = 0;
+  for (int c = 0; c < tn; ++c) {
+    int k = 0;  // band rows whose tile row reaches column c
+    for (int r = 0; r < h; ++r) k += sym_row_tiles(r0 + r, m, TM, TN) > c ? 1 : 0;
+    if (t < k) {
+      tj = c;
+      ti = r0 + (h - k) + t;
+      return;
+    }
+    t -= k;
   }
 }
 

@@ -1,0 +1,188 @@
+"""Host logic of the shape-adaptive kernel selection: the 256 x 384 configuration's tile orders
+and tile counts, launch signatures, and the tuning table (force, import, export).  CPU only:
+no call here launches a kernel."""
+
+from __future__ import annotations
+
+import itertools
+
+import pytest
+
+import newton_schulz_02_amd as nm
+
+WM, WN = 256, 384
+
+
+def cdiv(a, b):
+    return -(-a // b)
+
+
+def wide_sym_set(m):
+    """Brute force: the 256 x 384 tiles of an m x m output that hold an element on or below
+    the diagonal (row >= column)."""
+    out = set()
+    for i in range(cdiv(m, WM)):
+        last_row = min(i * WM + WM - 1, m - 1)
+        for j in range(cdiv(m, WN)):
+            if last_row >= j * WN:
+                out.add((i, j))
+    return out
+
+
+@pytest.mark.parametrize("m", [1, 100, 256, 257, 383, 384, 385, 640, 768, 1000, 1152, 4096, 11008])
+def test_wide_symmetric_order_covers_the_triangle_once(m):
+    order = nm.wide_tile_order(True, m)
+    assert len(order) == len(set(order))
+    assert set(order) == wide_sym_set(m)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (100, 300), (300, 100), (256, 384), (257, 385),
+                                       (4096, 11008), (11008, 4096), (640, 640)])
+def test_wide_full_order_is_a_bijection(rows, cols):
+    order = nm.wide_tile_order(False, rows, cols)
+    grid = set(itertools.product(range(cdiv(rows, WM)), range(cdiv(cols, WN))))
+    assert len(order) == len(grid) and set(order) == grid
+
+
+def _signature_groups(sig):
+    dtype, *groups = sig.split("|")
+    out = []
+    for g in groups:
+        kind, tri, nmflag, shapes = g.split(":", 3)
+        for item in shapes.split(":"):
+            shape, count = item.split("*")
+            m, n = (int(x) for x in shape.split("x"))
+            out.append((int(kind), int(tri), int(nmflag), m, n, int(count)))
+    return dtype, out
+
+
+def _expected_tiles(groups):
+    sq = wide = 0
+    for kind, tri, nmflag, m, n, count in groups:
+        if tri:
+            t = cdiv(m, 256)
+            sq += count * t * (t + 1) // 2
+            wide += count * len(wide_sym_set(m))
+            continue
+        # Full outputs are m x n: the restart product Q X and the update (n x m for the update
+        # of a transposed tall matrix).
+        assert kind in (3, 4)
+        rows, cols = m, n
+        if nmflag:
+            rows, cols = cols, rows
+        sq += count * cdiv(rows, 256) * cdiv(cols, 256)
+        wide += count * cdiv(rows, WM) * cdiv(cols, WN)
+    return sq, wide
+
+
+@pytest.mark.parametrize("shapes", [
+    [(300, 100), (100, 300), (640, 640)],
+    [(4096, 4096)] * 4 + [(4096, 11008)] * 2 + [(11008, 4096)],
+    [(1000, 700), (700, 1000), (129, 1), (1, 129), (2048, 6000)],
+])
+def test_tile_counts_of_both_configurations(shapes):
+    arr = nm.shape_array(shapes)
+    d = nm.plan_describe(arr, len(shapes), nm.make_hparams())
+    gemms = [L for L in d["launches"] if L["kind"] == "gemm"]
+    assert gemms
+    for L in gemms:
+        dtype, groups = _signature_groups(L["signature"])
+        assert dtype == "bf16"
+        assert sum(c for *_, c in groups) >= 1
+        assert tuple(L["tiles_cfg"]) == _expected_tiles(groups), L["signature"]
+        assert L["cfg"] == 0 and L["tiles"] == L["tiles_cfg"][0]
+
+
+def test_nm_flag_marks_the_transposed_tall_update():
+    d = nm.plan_describe(nm.shape_array([(300, 100)]), 1, nm.make_hparams())
+    last = [L for L in d["launches"] if L["kind"] == "gemm"][-1]
+    assert last["signature"] == "bf16|4:0:1:100x300*1"
+    d = nm.plan_describe(nm.shape_array([(100, 300)]), 1, nm.make_hparams())
+    last = [L for L in d["launches"] if L["kind"] == "gemm"][-1]
+    assert last["signature"] == "bf16|4:0:0:100x300*1"
+
+
+def test_fp32_signatures_name_their_dtype():
+    d = nm.plan_describe(nm.shape_array([(300, 200)], dtype=nm.MUON_F32), 1, nm.make_hparams())
+    sigs = [L["signature"] for L in d["launches"] if L["kind"] == "gemm"]
+    assert sigs and all(s.startswith("f32|") for s in sigs)
+
+
+@pytest.fixture
+def clean_table():
+    nm.tune_clear()
+    nm.tune_force(None)
+    yield
+    nm.tune_clear()
+    nm.tune_force(None)
+
+
+def _cfgs(shapes):
+    d = nm.plan_describe(nm.shape_array(shapes), len(shapes), nm.make_hparams())
+    return [(L["signature"], L["cfg"], L["tiles"], L["tiles_cfg"]) for L in d["launches"]
+            if L["kind"] == "gemm"]
+
+
+def test_table_and_force_select_the_configuration(clean_table):
+    shapes = [(640, 640), (300, 100)]
+    base = _cfgs(shapes)
+    assert all(c == 0 for _, c, _, _ in base)
+    # One signature to the wide configuration: only launches with that signature change.
+    sig = base[0][0]
+    nm.tune_import(f"{sig} 1\n")
+    assert nm.tune_table() == {sig: 1}
+    for s, c, tiles, tcfg in _cfgs(shapes):
+        assert c == (1 if s == sig else 0)
+        assert tiles == tcfg[c]
+    nm.tune_force(nm.CFG_WIDE)
+    assert all(c == 1 for _, c, _, _ in _cfgs(shapes))
+    nm.tune_force(nm.CFG_SQUARE)
+    assert all(c == 0 for _, c, _, _ in _cfgs(shapes))
+    nm.tune_force(None)
+    assert [c for _, c, _, _ in _cfgs(shapes)] == [1 if s == sig else 0 for s, *_ in base]
+
+
+def test_export_import_round_trip(clean_table):
+    assert nm.tune_export() == ""
+    text = "bf16|0:1:0:640x640*1 1\nbf16|4:0:1:100x300*1 0\nf32|2:1:0:64x64*3 1\n"
+    nm.tune_import(text)
+    out = nm.tune_export()
+    assert sorted(out.splitlines()) == sorted(text.splitlines())
+    assert out == "".join(sorted(ln + "\n" for ln in text.splitlines()))  # sorted by signature
+    nm.tune_clear()
+    nm.tune_import(out)
+    assert nm.tune_export() == out
+    # Overwrite and blank lines.
+    nm.tune_import("\nbf16|0:1:0:640x640*1 0\n\n")
+    assert nm.tune_table()["bf16|0:1:0:640x640*1"] == 0
+
+
+@pytest.mark.parametrize("bad", ["sig", "sig 2", "sig -1", " 1", "a b 1", "sig 1x", "sig "])
+def test_malformed_import_adds_nothing(clean_table, bad):
+    nm.tune_import("keep 1\n")
+    with pytest.raises(nm.MuonError):
+        nm.tune_import(f"new 0\n{bad}\n")
+    assert nm.tune_table() == {"keep": 1}
+
+
+def test_argument_errors(clean_table):
+    for cfg in (-2, 2, 7):
+        with pytest.raises(nm.MuonError):
+            nm.tune_force(cfg)
+    hp = nm.make_hparams()
+    with pytest.raises(nm.MuonError):
+        nm.tune_raw(nm.shape_array([(64, 64)]), 1, hp, 0, 0, None, reps=0)
+
+
+def test_wide_configuration_is_off_for_operands_beyond_32_bit_offsets(clean_table):
+    """(d + 384) * round_up(d, 128) * 2 >= 2^31 for d = 32768 (bf16); d = 32000 fits."""
+    nm.tune_force(nm.CFG_WIDE)
+    for d, ok in ((32000, True), (32768, False)):
+        shapes = [(d, d), (256, 512)]
+        desc = nm.plan_describe(nm.shape_array(shapes), 2, nm.make_hparams())
+        for L in desc["launches"]:
+            if L["kind"] != "gemm":
+                continue
+            has_big = f"{d}x{d}" in L["signature"]
+            assert L["wide_ok"] == (ok or not has_big)
+            assert L["cfg"] == (1 if L["wide_ok"] else 0)
