@@ -48,21 +48,26 @@ def kernel_hash(kernel: str = "gemm_bf16") -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel: str, workload: str):
-    """HBM bytes per launch of an MFMA kernel from the committed counter summary.
+def traffic_from_profiles(kernel: str, workload: str, launches: list[int]):
+    """HBM bytes per launch of an MFMA kernel, from the committed counter summary.
 
-    The summary records the kernel source hash it was taken with; a different hash means
-    the kernel changed since, and the figure is withheld (None).
+    The summary lists, per kernel, the bytes of each MFMA launch of the workload's plan (in
+    plan order) and the kernel's source hash.  ``launches`` are the plan indices the kernel
+    ran; the result is the mean of their bytes.  A hash that differs from the sources' means
+    the kernel changed since the counters were taken: the figure is withheld (None).
     """
-    path = ROOT / "profiles" / f"{kernel}_{workload}_hbm_traffic.md"
-    if not path.exists():
+    path = ROOT / "profiles" / f"gemm_{workload}_hbm_traffic.md"
+    if not path.exists() or not launches:
         return None
     text = path.read_text()
-    m_hash = re.search(r"kernel_hash:\s*([0-9a-f]+)", text)
-    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_hash = re.search(rf"^kernel_hash {kernel}:\s*([0-9a-f]+)", text, re.M)
+    m_bytes = re.search(rf"^launch_bytes {kernel}:\s*([0-9.eE+, ]+)$", text, re.M)
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash(kernel):
         return None
-    return float(m_bytes.group(1))
+    per_launch = [float(x) for x in m_bytes.group(1).split(",")]
+    if max(launches) >= len(per_launch):
+        return None
+    return sum(per_launch[i] for i in launches) / len(launches)
 
 
 def cpu_baseline(wl, budget_s: float = 30.0):
@@ -137,7 +142,7 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--kernel", choices=["tuned", "square", "wide"], default="tuned",
                     help="MFMA kernel per launch: measured at set-up (tuned) or one fixed")
-    ap.add_argument("--tune-reps", type=int, default=3)
+    ap.add_argument("--tune-reps", type=int, default=5)
     ap.add_argument("--tune-cache", default="", metavar="FILE",
                     help="tuning table to load before set-up (if it exists) and save after")
     args = ap.parse_args()
@@ -220,7 +225,9 @@ def main() -> int:
     avg_ms = gs["ms"] / gs["launches"]
     flops_per_launch = gs["flops"] / gs["launches"]
     achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
-    traffic = traffic_from_profiles(gemm_name, wl.name)
+    wide_dominant = gemm_name.startswith("gemm_wide")
+    traffic = traffic_from_profiles(gemm_name, wl.name,
+                                    [i for i, c in enumerate(cfg_of_launch) if bool(c) == wide_dominant])
     kernels = {k: {"launches": v["launches"] // args.steps, "ms_per_step": v["ms"] / args.steps,
                    "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None,
                    "gbs": (v["bytes"] / (v["ms"] * 1e-3) / 1e9) if v["bytes"] else None}

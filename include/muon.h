@@ -153,11 +153,14 @@ int muon_owner_assign(const double* cost, int32_t count, int32_t ranks, int64_t 
  * runs configuration 0, whatever the table or muon_tune_force say.
  *
  * muon_tune: runs one step over device copies of the list's params and momenta (the
- *   caller's matrices are not modified), and after each MFMA launch of that step times the
- *   same launch `reps` (>= 1) times under each configuration.  The fastest is stored under
- *   the launch's signature.  A set-up call: it allocates the copies with hipMalloc, frees
- *   them before returning and synchronises the stream.  Arguments and errors as muon_step,
- *   plus MUON_EINVAL for reps < 1 and MUON_EHIP when the copies cannot be allocated.
+ *   caller's matrices are not modified).  After each MFMA launch of that step it times the
+ *   same launch in `reps` rounds (1 <= reps <= 64), each round running it once under every
+ *   configuration.  The configuration with the smallest median time is stored under the
+ *   launch's signature; configuration 1 only when its median is at least 1 % below
+ *   configuration 0's.  A set-up call: it allocates the copies with hipMalloc, frees them
+ *   before returning and synchronises the stream.  Arguments and errors as muon_step, plus
+ *   MUON_EINVAL for reps outside [1, 64] and MUON_EHIP when the copies cannot be
+ *   allocated.
  * muon_tune_force: cfg in {0, 1} forces that configuration for every launch, -1 restores
  *   the table.  MUON_EINVAL for other values.  For tests and measurements.
  * muon_tune_clear: empties the table.

@@ -202,7 +202,7 @@ def step_raw(arr, count: int, hp: muon_hparams, ws_ptr: int, ws_bytes: int, stre
 
 
 def tune_raw(arr, count: int, hp: muon_hparams, ws_ptr: int, ws_bytes: int, stream_ptr,
-             reps: int = 3) -> None:
+             reps: int = 5) -> None:
     _check(lib().muon_tune(arr, int(count), ctypes.byref(hp), c_void_p(ws_ptr), int(ws_bytes),
                            stream_ptr, int(reps)))
 
@@ -296,7 +296,7 @@ class MuonStep:
         step_raw(self.arr, self.count, self.hp, self.workspace.data_ptr(), self.workspace.numel(),
                  _stream_handle(stream, self.device))
 
-    def tune(self, stream=None, reps: int = 3) -> None:
+    def tune(self, stream=None, reps: int = 5) -> None:
         """Time every MFMA launch of this step under each kernel configuration and cache the
         fastest (``muon_tune``); runs on copies, so params and momenta are unchanged."""
         tune_raw(self.arr, self.count, self.hp, self.workspace.data_ptr(), self.workspace.numel(),

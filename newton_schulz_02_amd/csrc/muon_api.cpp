@@ -3,6 +3,7 @@
 // update once; §2.2: Gram Newton-Schulz with the symmetric path and shape batching).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -325,7 +326,7 @@ int muon_step(const muon_matrix* mats, int32_t count, const muon_hparams* hp, vo
 int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, void* workspace,
               size_t workspace_bytes, void* hip_stream, int32_t reps) {
   try {
-    if (reps < 1) return fail(MUON_EINVAL, "reps must be >= 1");
+    if (reps < 1 || reps > 64) return fail(MUON_EINVAL, "reps must be in [1, 64]");
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     std::lock_guard<std::mutex> lock(g_mu);
     {  // validate the caller's list as muon_step would (host only)
@@ -380,34 +381,42 @@ int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, vo
     float* partials = reinterpret_cast<float*>(ws + plan.partial_off);
     const bool prof = g_prof;
     g_prof = false;  // the trial launches are not part of a profile
-    hipEvent_t ev[2] = {nullptr, nullptr};
-    e = hipEventCreate(&ev[0]);
-    if (e == hipSuccess) e = hipEventCreate(&ev[1]);
-    // Every launch runs once in order, so that each sees the operands of a real step; then
-    // each MFMA launch is timed under every kernel configuration, reps launches each.  The
-    // kernels' run time does not depend on the values, so the trials' repeated in-place
-    // writes do not bias the later timings.
+    // Two events per trial: rounds x configurations trials per launch.
+    std::vector<hipEvent_t> ev(size_t(2 * reps * kNumCfg), nullptr);
+    for (size_t i = 0; i < ev.size() && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
+    // Every launch runs once in order, so that each sees the operands of a real step.  Then
+    // each MFMA launch is timed in `reps` rounds; a round runs it once under every kernel
+    // configuration, so clock drift affects all of them alike.  The configuration with the
+    // smallest median wins, and a non-default one only when it is at least kTuneMargin
+    // faster: near-ties keep the default, so repeated tunings agree.  The kernels' run time
+    // does not depend on the values, so the trials' repeated in-place writes do not bias
+    // later timings.
+    constexpr float kTuneMargin = 0.01f;
     for (const PlanLaunch& L : plan.launches) {
       if (e != hipSuccess || rc != MUON_OK) break;
       rc = run_launch(dev, s, plan, L, kCfgSquare, ddesc, scale, partials, hp, count);
       if (rc != MUON_OK || L.kind != kLaunchGemm) continue;
-      float best = 0.0f;
-      int best_cfg = kCfgSquare;
-      for (int cfg = 0; cfg < kNumCfg && rc == MUON_OK && e == hipSuccess; ++cfg) {
-        if (cfg == kCfgWide && !L.wide_ok) continue;
-        e = hipEventRecord(ev[0], s);
-        for (int r = 0; r < reps && rc == MUON_OK && e == hipSuccess; ++r)
-          rc = run_launch(dev, s, plan, L, cfg, ddesc, scale, partials, hp, count);
-        if (e == hipSuccess) e = hipEventRecord(ev[1], s);
-        if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
-        float ms = 0.0f;
-        if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
-        if (e == hipSuccess && rc == MUON_OK && (cfg == kCfgSquare || ms < best)) {
-          best = ms;
-          best_cfg = cfg;
+      const int ncfg = L.wide_ok ? kNumCfg : 1;
+      for (int r = 0; r < reps && rc == MUON_OK && e == hipSuccess; ++r)
+        for (int cfg = 0; cfg < ncfg && rc == MUON_OK && e == hipSuccess; ++cfg) {
+          hipEvent_t* pair = &ev[size_t(2 * (r * kNumCfg + cfg))];
+          e = hipEventRecord(pair[0], s);
+          if (e == hipSuccess) rc = run_launch(dev, s, plan, L, cfg, ddesc, scale, partials, hp, count);
+          if (e == hipSuccess && rc == MUON_OK) e = hipEventRecord(pair[1], s);
         }
+      if (e == hipSuccess && rc == MUON_OK) e = hipStreamSynchronize(s);
+      float med[kNumCfg] = {0.0f, 0.0f};
+      for (int cfg = 0; cfg < ncfg && e == hipSuccess; ++cfg) {
+        std::vector<float> t(size_t(reps), 0.0f);
+        for (int r = 0; r < reps && e == hipSuccess; ++r)
+          e = hipEventElapsedTime(&t[size_t(r)], ev[size_t(2 * (r * kNumCfg + cfg))],
+                                  ev[size_t(2 * (r * kNumCfg + cfg)) + 1]);
+        std::sort(t.begin(), t.end());
+        med[cfg] = reps % 2 ? t[size_t(reps / 2)] : 0.5f * (t[size_t(reps / 2) - 1] + t[size_t(reps / 2)]);
       }
-      if (e == hipSuccess && rc == MUON_OK) g_tune[L.signature] = best_cfg;
+      if (e == hipSuccess && rc == MUON_OK)
+        g_tune[L.signature] = (ncfg > 1 && med[kCfgWide] < (1.0f - kTuneMargin) * med[kCfgSquare])
+                                  ? int(kCfgWide) : int(kCfgSquare);
     }
     g_prof = prof;
     const hipError_t es = hipStreamSynchronize(s);  // before the copies are freed

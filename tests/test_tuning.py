@@ -170,8 +170,9 @@ def test_argument_errors(clean_table):
         with pytest.raises(nm.MuonError):
             nm.tune_force(cfg)
     hp = nm.make_hparams()
-    with pytest.raises(nm.MuonError):
-        nm.tune_raw(nm.shape_array([(64, 64)]), 1, hp, 0, 0, None, reps=0)
+    for reps in (0, 65):
+        with pytest.raises(nm.MuonError):
+            nm.tune_raw(nm.shape_array([(64, 64)]), 1, hp, 0, 0, None, reps=reps)
 
 
 def test_wide_configuration_is_off_for_operands_beyond_32_bit_offsets(clean_table):
