@@ -140,8 +140,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
-    ap.add_argument("--kernel", choices=["tuned", "square", "wide"], default="tuned",
-                    help="MFMA kernel per launch: measured at set-up (tuned) or one fixed")
+    ap.add_argument("--kernel", choices=["tuned", "square", "wide", "square-split", "wide-split"],
+                    default="tuned",
+                    help="MFMA kernel configuration per launch: measured at set-up (tuned) or "
+                         "one fixed (256x256 or 256x384 tiles, optionally with the tail split)")
     ap.add_argument("--tune-reps", type=int, default=5)
     ap.add_argument("--tune-cache", default="", metavar="FILE",
                     help="tuning table to load before set-up (if it exists) and save after")
@@ -183,7 +185,8 @@ def main() -> int:
 
     # Set-up, untimed: pick the MFMA kernel configuration of each launch.
     t0 = time.perf_counter()
-    nm.tune_force({"tuned": None, "square": nm.CFG_SQUARE, "wide": nm.CFG_WIDE}[args.kernel])
+    nm.tune_force({"tuned": None, "square": nm.CFG_SQUARE, "wide": nm.CFG_WIDE,
+                   "square-split": nm.CFG_SQUARE_SPLIT, "wide-split": nm.CFG_WIDE_SPLIT}[args.kernel])
     cache = Path(args.tune_cache) if args.tune_cache else None
     if args.kernel == "tuned":
         if cache and cache.exists():
@@ -227,7 +230,7 @@ def main() -> int:
     achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
     wide_dominant = gemm_name.startswith("gemm_wide")
     traffic = traffic_from_profiles(gemm_name, wl.name,
-                                    [i for i, c in enumerate(cfg_of_launch) if bool(c) == wide_dominant])
+                                    [i for i, c in enumerate(cfg_of_launch) if bool(c & 1) == wide_dominant])
     kernels = {k: {"launches": v["launches"] // args.steps, "ms_per_step": v["ms"] / args.steps,
                    "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None,
                    "gbs": (v["bytes"] / (v["ms"] * 1e-3) / 1e9) if v["bytes"] else None}
@@ -264,7 +267,7 @@ def main() -> int:
             "coeffs": list(wl.coeffs),
             "adamw_tail": wl.tail.numel if wl.tail else 0,
             "kernel_selection": args.kernel,
-            "mfma_kernel_per_launch": ["256x384" if c else "256x256" for c in cfg_of_launch],
+            "mfma_kernel_per_launch": [nm.CFG_LABELS[c] for c in cfg_of_launch],
         },
         "roofline": {
             "bound": "mfma",

@@ -143,26 +143,32 @@ int muon_owner_assign(const double* cost, int32_t count, int32_t ranks, int64_t 
 
 /* Shape-adaptive kernel selection (DMuon summary §2.4: the tile shape is searched per
  * target and matrix shape, and the best configuration is cached and reused by later steps).
- * The library has two MFMA kernel configurations: 0 = 256 x 256 output tiles, 1 = 256 x 384
- * output tiles (8 waves of 128 x 96).  Each MFMA launch of a plan has a signature string
+ * The library has four MFMA kernel configurations: 0 = 256 x 256 output tiles, 1 = 256 x 384
+ * output tiles (8 waves of 128 x 96), 2 and 3 = the same with the tail split: the tiles of
+ * a launch's last, partial round of workgroups (one per compute unit) are cut along the
+ * contraction into pieces run by the otherwise idle units, and the last piece of a tile to
+ * finish adds the others' fp32 partial sums in piece order (so results are deterministic,
+ * but they may differ from configurations 0 and 1 by the rounding of those additions).  A
+ * launch with no tail worth cutting runs 2 as 0 and 3 as 1.  Each MFMA launch of a plan has
+ * a signature string
  * (dtype, then per shape group its kind, symmetry, orientation and run-length shapes); a
  * process-wide table maps signatures to configurations, and muon_step uses configuration 0
  * for a signature the table does not hold.  The table is shared by all threads and devices.
  * Configuration 1 addresses operands with 32-bit offsets: a launch holding a matrix whose
  * larger side d has (d + 384) * (d rounded up to 128) * element size >= 2^31 bytes always
- * runs configuration 0, whatever the table or muon_tune_force say.
+ * runs configuration 0 (or 2), whatever the table or muon_tune_force say.
  *
  * muon_tune: runs one step over device copies of the list's params and momenta (the
  *   caller's matrices are not modified).  After each MFMA launch of that step it times the
  *   same launch in `reps` rounds (1 <= reps <= 64), each round running it once under every
- *   configuration.  The configuration with the smallest median time is stored under the
- *   launch's signature; configuration 1 only when its median is at least 1 % below
- *   configuration 0's.  A set-up call: it allocates the copies with hipMalloc, frees them
+ *   configuration that applies to it.  The configuration with the smallest median time is
+ *   stored under the launch's signature when its median is at least 1 % below
+ *   configuration 0's, else configuration 0.  A set-up call: it allocates the copies with hipMalloc, frees them
  *   before returning and synchronises the stream.  Arguments and errors as muon_step, plus
  *   MUON_EINVAL for reps outside [1, 64] and MUON_EHIP when the copies cannot be
  *   allocated.
- * muon_tune_force: cfg in {0, 1} forces that configuration for every launch, -1 restores
- *   the table.  MUON_EINVAL for other values.  For tests and measurements.
+ * muon_tune_force: cfg in {0, 1, 2, 3} forces that configuration for every launch, -1
+ *   restores the table.  MUON_EINVAL for other values.  For tests and measurements.
  * muon_tune_clear: empties the table.
  * muon_tune_export: writes the table as text, one "signature cfg" line per entry, sorted,
  *   NUL-terminated, into buf (len bytes).  *needed (may be NULL) receives the size with the
@@ -206,6 +212,15 @@ int muon_debug_xcd_remap(int total, int* out);
  * output: tri != 0 walks the 256 x 384 tiles that meet the lower triangle of a rows x rows
  * output (ti: 256-row band, tj: 384-column band).  Returns the tile count. */
 int muon_debug_wide_tile_order(int tri, int rows, int cols, int* ti, int* tj);
+/* muon_debug_split: the tail split of a launch of `tiles` tiles on `units` compute units
+ * whose tail tiles have `ksteps` k-steps each.  plan[0..5] receives the mode (0 none,
+ * 1 equal pieces, 2 one uneven cut), the pieces per tail tile (mode 1) or the cut's second
+ * pieces per unit (mode 2), the workgroups running whole tiles, the tail tiles, the tail
+ * workgroups and the partial-sum slots.  When items is not NULL, items[5 j .. 5 j + 4]
+ * receives, for tail workgroup j < max_items, its tail tile, piece, piece count and k-step
+ * range [k0, k1), or -1 in the first field for a workgroup without a piece.  Returns the
+ * number of tail workgroups, or MUON_EINVAL for a NULL plan or negative sizes. */
+int muon_debug_split(int tiles, int units, int ksteps, int* plan, int* items, int max_items);
 
 const char* muon_strerror(int status); /* static string */
 const char* muon_last_error(void);     /* detail of the last failure on this thread */

@@ -89,6 +89,7 @@ _SIGNATURES = {
     "muon_tune_export": (c_int, [c_char_p, c_size_t, POINTER(c_size_t)]),
     "muon_tune_import": (c_int, [c_char_p]),
     "muon_debug_wide_tile_order": (c_int, [c_int, c_int, c_int, POINTER(c_int), POINTER(c_int)]),
+    "muon_debug_split": (c_int, [c_int, c_int, c_int, POINTER(c_int), POINTER(c_int), c_int]),
 }
 
 _lib = None
@@ -207,7 +208,9 @@ def tune_raw(arr, count: int, hp: muon_hparams, ws_ptr: int, ws_bytes: int, stre
                            stream_ptr, int(reps)))
 
 
-CFG_SQUARE, CFG_WIDE = 0, 1  # MFMA kernel configurations: 256 x 256 and 256 x 384 tiles
+# MFMA kernel configurations: 256 x 256 and 256 x 384 tiles, each also with the tail split.
+CFG_SQUARE, CFG_WIDE, CFG_SQUARE_SPLIT, CFG_WIDE_SPLIT = 0, 1, 2, 3
+CFG_LABELS = {0: "256x256", 1: "256x384", 2: "256x256+split", 3: "256x384+split"}
 
 
 def tune_force(cfg) -> None:
@@ -339,6 +342,20 @@ def wide_tile_order(tri: bool, rows: int, cols: int = 0):
     ti, tj = (c_int * max(n, 1))(), (c_int * max(n, 1))()
     lib().muon_debug_wide_tile_order(int(bool(tri)), rows, cols, ti, tj)
     return list(zip(ti[:n], tj[:n]))
+
+
+def split_plan(tiles: int, units: int, ksteps: int):
+    """Test hook: the tail split of a launch.  Returns (plan dict, items) where items[j] is
+    (tile, piece, pieces, k0, k1) of tail workgroup j, or None for a padding workgroup."""
+    plan = (c_int * 6)()
+    n = lib().muon_debug_split(tiles, units, ksteps, plan, None, 0)
+    if n < 0:
+        _check(n)
+    items = (c_int * max(5 * n, 1))()
+    lib().muon_debug_split(tiles, units, ksteps, plan, items, n)
+    keys = ("mode", "pieces_or_n", "dp_tiles", "tail", "tail_wgs", "slots")
+    out = [None if items[5 * j] < 0 else tuple(items[5 * j:5 * j + 5]) for j in range(n)]
+    return dict(zip(keys, plan[:6])), out
 
 
 def xcd_remap(total: int):

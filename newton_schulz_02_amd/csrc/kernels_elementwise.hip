@@ -3,7 +3,8 @@
 //               M'^2 (wave64 shuffle reduction), and the zero-padded row / transposed
 //               copies that the MFMA phase reads (transpose staged through LDS so both
 //               the read and the write are coalesced);
-//   k_norm      s = 1 / (sqrt(sum of partials) + eps) per matrix, summed in a fixed order;
+//   k_norm      s = 1 / (sqrt(sum of partials) + eps) per matrix, summed in a fixed order
+//               (it also clears the contraction kernels' tail-split counters);
 //   k_adamw     AdamW on the packed fp32 tail.
 // Method: DMuon summary §1 (Newton-Schulz on momentum-aggregated gradients); MatrixFSDP
 // summary, Methodology §1 (AdamW for the non-matrix tail).
@@ -164,6 +165,10 @@ __global__ __launch_bounds__(256) void k_norm(NormArgs a) {
     __syncthreads();
   }
   if (threadIdx.x == 0) a.scale[blockIdx.x] = float(1.0 / (sqrt(red[0]) + double(a.eps)));
+  // The contractions' tail-split counters start every step at zero (each tile's last piece
+  // clears its own pair again when it is done).
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < a.split_cnt_n; i += 256) a.split_cnt[i] = 0;
 }
 
 __device__ __forceinline__ void adamw_one(float& p, float g, float& m, float& v, const AdamArgs& a) {

@@ -38,6 +38,7 @@
 #include <type_traits>
 
 #include "muon_internal.h"
+#include "split_fixup.h"
 #include "tile_order.h"
 
 using namespace muon;
@@ -196,8 +197,13 @@ __device__ __forceinline__ float tri_value(int kind, int gi, int gj, int m, floa
   return x;
 }
 
+// One output tile of the launch (logical tile `bid`), or piece `piece` of `pieces` of it when
+// the tail split cut its contraction (cnt: the tile's two split counters, slots: its
+// `pieces` partial-sum slots).
 template <typename S>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, const int piece,
+                                          const int pieces, int32_t* const cnt,
+                                          float* const slots) {
   __shared__ __attribute__((aligned(1024))) char lds0[kArrBytes];
   __shared__ __attribute__((aligned(1024))) char lds1[kArrBytes];
   __shared__ __attribute__((aligned(1024))) char lds2[kStages > 2 ? kArrBytes : 16];
@@ -212,7 +218,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
   };
 
   // ---- which group, matrix and tile --------------------------------------------------
-  const int bid = xcd_remap(int(blockIdx.x), int(gridDim.x));
   GroupArg g = args.g[0];
 #pragma unroll
   for (int q = 1; q < kMaxGroups; ++q)
@@ -269,6 +274,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
   // an instruction writes LDS bytes [16 l, 16 l + 16) of its 1 KB block: row l / kChunks
   // of the block, chunk position l % kChunks, holding global chunk (position ^ swz(row)).
   const int ksteps = ident ? 0 : A.kpad / Mma<S>::kStageK;
+  int k0 = 0, k1 = ksteps;  // the k-steps of this piece
+  if (pieces > 1) split_range(args.split_mode, args.split_n, ksteps, kSplitUnit, piece, pieces, k0, k1);
   const int64_t lda = A.ld * int64_t(sizeof(S));
   const int64_t ldb = B.ld * int64_t(sizeof(S));
   const int lrow = lane / kChunks;
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
   constexpr int kLoadsPerStage = 2 * kInstPerOperand;
   // Prologue: stages 0 .. kStages-2 in flight.
   static_for<0, kStages - 1>([&](auto sc) {
-    if (sc.value < ksteps) issue(sc.value, stage_of(sc));
+    if (k0 + sc.value < k1) issue(k0 + sc.value, stage_of(sc));
   });
 
   // Fragment rows of this lane (+ 32 i for A, + 32 j for B).
@@ -323,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
   auto kstep = [&](int ks, auto sc, auto pending) {
     wait_vm<decltype(pending)::value>();
     stage_barrier();  // all waves' loads of stage ks landed; stage ks-1 is free again
-    if (ks + kStages - 1 < ksteps)
+    if (ks + kStages - 1 < k1)
       issue(ks + kStages - 1, stage_of(std::integral_constant<int, decltype(sc)::value + kStages - 1>{}));
     if (idle) return;
     const char* st = stage_of(sc);
@@ -337,15 +344,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
         for (int j = 0; j < kFragN; ++j) Mma<S>::step(fa[i], fb[j], acc[i][j]);
     }
   };
-  // ksteps is a multiple of kStages (contraction dims are padded to kKPad).  Full blocks
-  // keep kStages-2 stages in flight behind the one being read; the last block drains.
-  int kb = 0;
-  for (; kb + kStages < ksteps; kb += kStages) {
+  // k0 and k1 are multiples of kStages (contraction dims are padded to kKPad, split pieces
+  // end on multiples of kSplitUnit).  Full blocks keep kStages-2 stages in flight behind the
+  // one being read; the last block drains.
+  int kb = k0;
+  for (; kb + kStages < k1; kb += kStages) {
     static_for<0, kStages>([&](auto sc) {
       kstep(kb + sc.value, sc, std::integral_constant<int, (kStages - 2) * kLoadsPerStage>{});
     });
   }
-  if (kb < ksteps) {
+  if (kb < k1) {
     static_for<0, kStages>([&](auto sc) {
       constexpr int left = kStages - 1 - decltype(sc)::value;   // stages after this one
       constexpr int ahead = left < kStages - 2 ? left : kStages - 2;
@@ -353,6 +361,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
     });
   }
   __syncthreads();  // the epilogue reuses the LDS
+  // A piece of a split tile: unless it is the tile's last to finish, it leaves its partial
+  // sums to that one; the last adds them in and stores the tile.
+  if (pieces > 1 &&
+      !split_fixup<4, kFragN>(acc, piece, pieces, cnt, slots, kSlotFloats,
+                              reinterpret_cast<int*>(lds0), idle))
+    return;
 
   // ---- epilogue ------------------------------------------------------------------------
   // acc[i][j][r] holds tile element (128 wm + 32 i + 8 (r/4) + 4 lk + r%4, 64 wn + 32 j + lr).
@@ -619,15 +633,36 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
   }
 }
 
+// The launch: workgroups [0, dp_tiles) run whole tiles in the XCD-aware order; with a tail
+// split the next tail_wgs run one piece each of the last tail_tiles tiles (tile_order.h).
+template <typename S>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
+  const int w = int(blockIdx.x);
+  int t = 0, piece = 0, pieces = 1;
+  int32_t* cnt = nullptr;
+  float* slots = nullptr;
+  if (w < args.dp_tiles) {
+    t = xcd_remap(w, args.dp_tiles);
+  } else {
+    if (!split_item(args.split_mode, args.tail_tiles, args.tail_wgs, args.split_c, w - args.dp_tiles, t,
+                    piece, pieces))
+      return;
+    cnt = args.split_cnt + 2 * t;
+    slots = args.split_slots + int64_t(t) * pieces * kSlotFloats;
+    t += args.dp_tiles;
+  }
+  gemm_tile<S>(args, t, piece, pieces, cnt, slots);
+}
+
 }  // namespace
 
 int muon_launch_gemm(const GemmArgs& a, int dtype, void* stream) {
-  if (a.total_tiles <= 0) return hipSuccess;
+  if (a.grid <= 0) return hipSuccess;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == kBF16)
-    hipLaunchKernelGGL(k_gemm<uint16_t>, dim3(a.total_tiles), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(k_gemm<uint16_t>, dim3(a.grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(k_gemm<float>, dim3(a.total_tiles), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(k_gemm<float>, dim3(a.grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

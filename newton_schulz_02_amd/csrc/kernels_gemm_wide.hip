@@ -35,6 +35,7 @@
 #include <type_traits>
 
 #include "muon_internal.h"
+#include "split_fixup.h"
 #include "tile_order.h"
 
 using namespace muon;
@@ -317,8 +318,13 @@ __device__ __attribute__((always_inline)) inline void ep_wave(f32x16 (&acc)[kFra
   }
 }
 
+// One output tile of the launch (logical tile `bid`), or piece `piece` of `pieces` of it when
+// the tail split cut its contraction (cnt: the tile's two split counters, slots: its
+// `pieces` partial-sum slots).
 template <typename S>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_wide(GemmArgs args) {
+__device__ __forceinline__ void gemm_wide_tile(const GemmArgs& args, const int bid, const int piece,
+                                               const int pieces, int32_t* const cnt,
+                                               float* const slots) {
   __shared__ __attribute__((aligned(1024))) char lds0[kArrBytes];
   __shared__ __attribute__((aligned(1024))) char lds1[kArrBytes];
   // Stage array s, named statically when s is a compile-time constant.
@@ -328,7 +334,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_wide(GemmArgs args) {
   };
 
   // ---- which group, matrix and tile --------------------------------------------------
-  const int bid = xcd_remap(int(blockIdx.x), int(gridDim.x));
   GroupArg g = args.g[0];
 #pragma unroll
   for (int q = 1; q < kMaxGroups; ++q)
@@ -391,6 +396,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_wide(GemmArgs args) {
   // past the end of an operand (offsets at or beyond its row count times its row pitch) read
   // as zeros.
   const int ksteps = ident ? 0 : A.kpad / Mma<S>::kStageK;
+  int k0 = 0, k1 = ksteps;  // the k-steps of this piece
+  if (pieces > 1) split_range(args.split_mode, args.split_n, ksteps, kSplitUnit, piece, pieces, k0, k1);
   const uint32_t lda = uint32_t(A.ld) * uint32_t(sizeof(S));
   const uint32_t ldb = uint32_t(B.ld) * uint32_t(sizeof(S));
   const int lrow = lane / kChunks;
@@ -424,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_wide(GemmArgs args) {
   };
   // Prologue: stages 0 .. kStages-2 in flight.
   static_for<0, kStages - 1>([&](auto sc) {
-    if (sc.value < ksteps) issue(sc.value, stage_of(sc));
+    if (k0 + sc.value < k1) issue(k0 + sc.value, stage_of(sc));
   });
 
   // Fragment rows of this lane (+ 32 i for A, + 32 j for B).
@@ -450,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_wide(GemmArgs args) {
   auto kstep = [&](int ks, auto sc, auto pending) __attribute__((always_inline)) {
     wait_vm<decltype(pending)::value>();
     stage_barrier();  // all waves' loads of stage ks landed; stage ks-1 is free again
-    if (ks + kStages - 1 < ksteps)
+    if (ks + kStages - 1 < k1)
       issue(ks + kStages - 1, stage_of(std::integral_constant<int, decltype(sc)::value + kStages - 1>{}));
     if (idle) return;
     const char* st = stage_of(sc);
@@ -465,15 +472,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_wide(GemmArgs args) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // ksteps is a multiple of kStages (contraction dims are padded to kKPad).  Full blocks
-  // keep kStages-2 stages in flight behind the one being read; the last block drains.
-  int kb = 0;
-  for (; kb + kStages < ksteps; kb += kStages) {
+  // k0 and k1 are multiples of kStages (contraction dims are padded to kKPad, split pieces
+  // end on multiples of kSplitUnit).  Full blocks keep kStages-2 stages in flight behind the
+  // one being read; the last block drains.
+  int kb = k0;
+  for (; kb + kStages < k1; kb += kStages) {
     static_for<0, kStages>([&](auto sc) {
       kstep(kb + sc.value, sc, std::integral_constant<int, (kStages - 2) * kLoadsPerStage>{});
     });
   }
-  if (kb < ksteps) {
+  if (kb < k1) {
     static_for<0, kStages>([&](auto sc) {
       constexpr int left = kStages - 1 - decltype(sc)::value;   // stages after this one
       constexpr int ahead = left < kStages - 2 ? left : kStages - 2;
@@ -481,6 +489,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_wide(GemmArgs args) {
     });
   }
   __syncthreads();  // the epilogue reuses the LDS
+  // A piece of a split tile: unless it is the tile's last to finish, it leaves its partial
+  // sums to that one; the last adds them in and stores the tile.
+  if (pieces > 1 &&
+      !split_fixup<kFragM, kFragN>(acc, piece, pieces, cnt, slots, kSlotFloats,
+                                   reinterpret_cast<int*>(lds0), idle))
+    return;
 
   // ---- epilogue ------------------------------------------------------------------------
   // acc[i][j][r] holds tile element (128 wm + 32 i + 8 (r/4) + 4 lk + r%4, 96 wn + 32 j + lr).
@@ -525,15 +539,36 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_wide(GemmArgs args) {
 
 }
 
+// The launch: workgroups [0, dp_tiles) run whole tiles in the XCD-aware order; with a tail
+// split the next tail_wgs run one piece each of the last tail_tiles tiles (tile_order.h).
+template <typename S>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_wide(GemmArgs args) {
+  const int w = int(blockIdx.x);
+  int t = 0, piece = 0, pieces = 1;
+  int32_t* cnt = nullptr;
+  float* slots = nullptr;
+  if (w < args.dp_tiles) {
+    t = xcd_remap(w, args.dp_tiles);
+  } else {
+    if (!split_item(args.split_mode, args.tail_tiles, args.tail_wgs, args.split_c, w - args.dp_tiles, t,
+                    piece, pieces))
+      return;
+    cnt = args.split_cnt + 2 * t;
+    slots = args.split_slots + int64_t(t) * pieces * kSlotFloats;
+    t += args.dp_tiles;
+  }
+  gemm_wide_tile<S>(args, t, piece, pieces, cnt, slots);
+}
+
 }  // namespace
 
 int muon_launch_gemm_wide(const GemmArgs& a, int dtype, void* stream) {
-  if (a.total_tiles <= 0) return hipSuccess;
+  if (a.grid <= 0) return hipSuccess;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == kBF16)
-    hipLaunchKernelGGL(k_gemm_wide<uint16_t>, dim3(a.total_tiles), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(k_gemm_wide<uint16_t>, dim3(a.grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(k_gemm_wide<float>, dim3(a.total_tiles), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(k_gemm_wide<float>, dim3(a.grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -45,6 +45,7 @@ struct Slot {
 struct DeviceState {
   bool checked = false;
   bool supported = false;
+  int units = kMaxUnits;  // compute units (the tail split plans for them)
   Slot ring[4];
   int next = 0;
 };
@@ -87,6 +88,7 @@ int check_device(int dev) {
     hipError_t e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
     st.supported = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    st.units = std::max(1, std::min(int(prop.multiProcessorCount), kMaxUnits));
     st.checked = true;
     if (!st.supported)
       t_last_error = std::string("device architecture ") + prop.gcnArchName + " is not gfx950";
@@ -162,8 +164,12 @@ int timed(int dev, hipStream_t s, const char* name, double flops, double bytes, 
 }
 
 // Enqueue one launch of the plan on stream s.  Caller holds g_mu.
-int run_launch(int dev, hipStream_t s, const Plan& plan, const PlanLaunch& L, int cfg, const MatDesc* ddesc,
-               float* scale, float* partials, const muon_hparams* hp, int count) {
+int run_launch(int dev, hipStream_t s, const Plan& plan, const PlanLaunch& L, int cfg, char* ws,
+               const muon_hparams* hp, int count) {
+  const MatDesc* ddesc = reinterpret_cast<const MatDesc*>(ws + plan.desc_off);
+  float* scale = reinterpret_cast<float*>(ws + plan.scale_off);
+  float* partials = reinterpret_cast<float*>(ws + plan.partial_off);
+  int32_t* split_cnt = reinterpret_cast<int32_t*>(ws + plan.split_cnt_off);
   if (L.kind == kLaunchMomentum) {
     MomArgs a;
     a.desc = ddesc;
@@ -183,6 +189,8 @@ int run_launch(int dev, hipStream_t s, const Plan& plan, const PlanLaunch& L, in
     a.scale = scale;
     a.count = count;
     a.eps = hp->eps;
+    a.split_cnt = split_cnt;
+    a.split_cnt_n = plan.split_cnt_n;
     return timed(dev, s, "norm", 0.0, 0.0, [&] { return muon_launch_norm(a, s); });
   }
   GemmArgs a;
@@ -192,12 +200,26 @@ int run_launch(int dev, hipStream_t s, const Plan& plan, const PlanLaunch& L, in
   a.pa = hp->ns_a;
   a.pb = hp->ns_b;
   a.pc = hp->ns_c;
-  const std::vector<GroupArg>& groups = L.groups_cfg[cfg];
+  const int shape = cfg_shape(cfg);
+  const std::vector<GroupArg>& groups = L.groups_cfg[shape];
   a.ngroups = int32_t(groups.size());
-  a.total_tiles = int32_t(L.tiles_cfg[cfg]);
+  a.total_tiles = int32_t(L.tiles_cfg[shape]);
   for (size_t g = 0; g < groups.size(); ++g) a.g[g] = groups[g];
+  const SplitPlan& sp = L.split_cfg[shape];
+  const bool split = cfg_split(cfg) && sp.mode != kSplitNone;
+  a.dp_tiles = split ? sp.dp_tiles : a.total_tiles;
+  a.split_mode = split ? sp.mode : int(kSplitNone);
+  a.split_c = sp.c;
+  a.split_n = sp.n;
+  a.tail_tiles = split ? sp.tail : 0;
+  a.tail_wgs = split ? sp.tail_wgs : 0;
+  a.split_cnt = split_cnt;
+  a.split_slots = reinterpret_cast<float*>(ws + plan.split_slot_off);
+  a.grid = a.dp_tiles + a.tail_wgs;
+  if (split && (sp.tail > plan.split_cnt_n / 2 || sp.slots > plan.split_slots))
+    return fail(MUON_EINVAL, "internal: tail split exceeds its workspace");
   const bool bf = L.dtype == kBF16;
-  if (cfg == kCfgWide)
+  if (shape == kCfgWide)
     return timed(dev, s, bf ? "gemm_wide_bf16" : "gemm_wide_f32", L.flops, 0.0,
                  [&] { return muon_launch_gemm_wide(a, L.dtype, s); });
   return timed(dev, s, bf ? "gemm_bf16" : "gemm_f32", L.flops, 0.0,
@@ -226,6 +248,7 @@ int prepare(const muon_matrix* mats, int32_t count, const muon_hparams* hp, void
   fill_descs(*plan, mats, hp, ws, &descs);
   if ((rc = current_device(dev)) != MUON_OK) return rc;
   if ((rc = check_device(*dev)) != MUON_OK) return rc;
+  if (g_dev[*dev].units != plan->units) plan_splits(plan, g_dev[*dev].units);
   return upload(*dev, descs.data(), descs.size() * sizeof(MatDesc), ws + plan->desc_off, s);
 }
 
@@ -310,11 +333,8 @@ int muon_step(const muon_matrix* mats, int32_t count, const muon_hparams* hp, vo
     int rc = prepare(mats, count, hp, workspace, workspace_bytes, s, &plan, &dev);
     if (rc != MUON_OK || count == 0) return rc;
     char* ws = static_cast<char*>(workspace);
-    const MatDesc* ddesc = reinterpret_cast<const MatDesc*>(ws + plan.desc_off);
-    float* scale = reinterpret_cast<float*>(ws + plan.scale_off);
-    float* partials = reinterpret_cast<float*>(ws + plan.partial_off);
     for (const PlanLaunch& L : plan.launches) {
-      rc = run_launch(dev, s, plan, L, L.cfg, ddesc, scale, partials, hp, count);
+      rc = run_launch(dev, s, plan, L, L.cfg, ws, hp, count);
       if (rc != MUON_OK) return rc;
     }
     return MUON_OK;
@@ -366,7 +386,7 @@ int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, vo
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (tuning copies)");
 
     const int saved_force = g_force_cfg;
-    g_force_cfg = kCfgSquare;  // the plan's own groups are the square ones; trials use both
+    g_force_cfg = kCfgSquare;  // the plan's own groups are the square ones; trials use all
     Plan plan;
     int dev = 0;
     int rc = prepare(shadow.data(), count, hp, workspace, workspace_bytes, s, &plan, &dev);
@@ -376,9 +396,6 @@ int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, vo
       return rc;
     }
     char* ws = static_cast<char*>(workspace);
-    const MatDesc* ddesc = reinterpret_cast<const MatDesc*>(ws + plan.desc_off);
-    float* scale = reinterpret_cast<float*>(ws + plan.scale_off);
-    float* partials = reinterpret_cast<float*>(ws + plan.partial_off);
     const bool prof = g_prof;
     g_prof = false;  // the trial launches are not part of a profile
     // Two events per trial: rounds x configurations trials per launch.
@@ -386,27 +403,33 @@ int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, vo
     for (size_t i = 0; i < ev.size() && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
     // Every launch runs once in order, so that each sees the operands of a real step.  Then
     // each MFMA launch is timed in `reps` rounds; a round runs it once under every kernel
-    // configuration, so clock drift affects all of them alike.  The configuration with the
-    // smallest median wins, and a non-default one only when it is at least kTuneMargin
-    // faster: near-ties keep the default, so repeated tunings agree.  The kernels' run time
-    // does not depend on the values, so the trials' repeated in-place writes do not bias
-    // later timings.
+    // configuration that applies to it (the 256 x 384 tiles when its operands fit their
+    // offsets, the tail split when it has a tail to cut), so clock drift affects all of
+    // them alike.  The configuration with the smallest median wins, and a non-default one
+    // only when it is at least kTuneMargin faster than the default: near-ties keep the
+    // default, so repeated tunings agree.  The kernels' run time does not depend on the
+    // values, so the trials' repeated in-place writes do not bias later timings.
     constexpr float kTuneMargin = 0.01f;
     for (const PlanLaunch& L : plan.launches) {
       if (e != hipSuccess || rc != MUON_OK) break;
-      rc = run_launch(dev, s, plan, L, kCfgSquare, ddesc, scale, partials, hp, count);
+      rc = run_launch(dev, s, plan, L, kCfgSquare, ws, hp, count);
       if (rc != MUON_OK || L.kind != kLaunchGemm) continue;
-      const int ncfg = L.wide_ok ? kNumCfg : 1;
+      bool valid[kNumCfg];
+      for (int cfg = 0; cfg < kNumCfg; ++cfg)
+        valid[cfg] = (cfg_shape(cfg) != kCfgWide || L.wide_ok) &&
+                     (!cfg_split(cfg) || L.split_cfg[cfg_shape(cfg)].mode != kSplitNone);
       for (int r = 0; r < reps && rc == MUON_OK && e == hipSuccess; ++r)
-        for (int cfg = 0; cfg < ncfg && rc == MUON_OK && e == hipSuccess; ++cfg) {
+        for (int cfg = 0; cfg < kNumCfg && rc == MUON_OK && e == hipSuccess; ++cfg) {
+          if (!valid[cfg]) continue;
           hipEvent_t* pair = &ev[size_t(2 * (r * kNumCfg + cfg))];
           e = hipEventRecord(pair[0], s);
-          if (e == hipSuccess) rc = run_launch(dev, s, plan, L, cfg, ddesc, scale, partials, hp, count);
+          if (e == hipSuccess) rc = run_launch(dev, s, plan, L, cfg, ws, hp, count);
           if (e == hipSuccess && rc == MUON_OK) e = hipEventRecord(pair[1], s);
         }
       if (e == hipSuccess && rc == MUON_OK) e = hipStreamSynchronize(s);
-      float med[kNumCfg] = {0.0f, 0.0f};
-      for (int cfg = 0; cfg < ncfg && e == hipSuccess; ++cfg) {
+      float med[kNumCfg] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int cfg = 0; cfg < kNumCfg && e == hipSuccess; ++cfg) {
+        if (!valid[cfg]) continue;
         std::vector<float> t(size_t(reps), 0.0f);
         for (int r = 0; r < reps && e == hipSuccess; ++r)
           e = hipEventElapsedTime(&t[size_t(r)], ev[size_t(2 * (r * kNumCfg + cfg))],
@@ -414,9 +437,12 @@ int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, vo
         std::sort(t.begin(), t.end());
         med[cfg] = reps % 2 ? t[size_t(reps / 2)] : 0.5f * (t[size_t(reps / 2) - 1] + t[size_t(reps / 2)]);
       }
-      if (e == hipSuccess && rc == MUON_OK)
-        g_tune[L.signature] = (ncfg > 1 && med[kCfgWide] < (1.0f - kTuneMargin) * med[kCfgSquare])
-                                  ? int(kCfgWide) : int(kCfgSquare);
+      if (e == hipSuccess && rc == MUON_OK) {
+        int best = kCfgSquare;
+        for (int cfg = 1; cfg < kNumCfg; ++cfg)
+          if (valid[cfg] && med[cfg] < med[best]) best = cfg;
+        g_tune[L.signature] = med[best] < (1.0f - kTuneMargin) * med[kCfgSquare] ? best : int(kCfgSquare);
+      }
     }
     g_prof = prof;
     const hipError_t es = hipStreamSynchronize(s);  // before the copies are freed
@@ -431,8 +457,29 @@ int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, vo
   }
 }
 
+int muon_debug_split(int tiles, int units, int ksteps, int* plan, int* items, int max_items) {
+  if (!plan || tiles < 0 || units < 1 || ksteps < 0 || max_items < 0)
+    return fail(MUON_EINVAL, "muon_debug_split: bad arguments");
+  const SplitPlan sp = plan_split(tiles, units, ksteps, kSplitUnit);
+  const int out[6] = {sp.mode, sp.mode == kSplitEqual ? sp.c : sp.n, sp.dp_tiles, sp.tail,
+                      sp.tail_wgs, sp.slots};
+  std::memcpy(plan, out, sizeof out);
+  for (int j = 0; items && j < sp.tail_wgs && j < max_items; ++j) {
+    int t, piece, pieces, k0 = 0, k1 = 0;
+    if (!split_item(sp.mode, sp.tail, sp.tail_wgs, sp.c, j, t, piece, pieces)) {
+      const int none[5] = {-1, -1, -1, -1, -1};
+      std::memcpy(items + 5 * j, none, sizeof none);
+      continue;
+    }
+    split_range(sp.mode, sp.n, ksteps, kSplitUnit, piece, pieces, k0, k1);
+    const int it[5] = {t, piece, pieces, k0, k1};
+    std::memcpy(items + 5 * j, it, sizeof it);
+  }
+  return sp.tail_wgs;
+}
+
 int muon_tune_force(int32_t cfg) {
-  if (cfg < -1 || cfg >= kNumCfg) return fail(MUON_EINVAL, "cfg must be -1, 0 or 1");
+  if (cfg < -1 || cfg >= kNumCfg) return fail(MUON_EINVAL, "cfg must be -1, 0, 1, 2 or 3");
   std::lock_guard<std::mutex> lock(g_mu);
   g_force_cfg = cfg;
   return MUON_OK;
@@ -467,9 +514,10 @@ int muon_tune_import(const char* text) {
     if (sp == std::string::npos || sp == 0 || sp + 1 >= line.size())
       return fail(MUON_EINVAL, "tuning line without 'signature cfg': " + line);
     const std::string sig = line.substr(0, sp), val = line.substr(sp + 1);
-    if (sig.find(' ') != std::string::npos || (val != "0" && val != "1"))
+    if (sig.find(' ') != std::string::npos || val.size() != 1 || val[0] < '0' ||
+        val[0] >= char('0' + kNumCfg))
       return fail(MUON_EINVAL, "bad tuning line: " + line);
-    add[sig] = val == "1" ? kCfgWide : kCfgSquare;
+    add[sig] = val[0] - '0';
   }
   std::lock_guard<std::mutex> lock(g_mu);
   for (const auto& kv : add) g_tune[kv.first] = kv.second;

@@ -18,8 +18,22 @@ namespace muon {
 constexpr int kTile = 256;       // output tile edge of the square-tile MFMA kernel
 constexpr int kWideM = 256;      // output tile rows of the wide-tile MFMA kernel
 constexpr int kWideN = 384;      // output tile columns of the wide-tile MFMA kernel
-// MFMA kernel configurations (chosen per launch: tuned, or the square one by default).
-enum GemmCfg : int32_t { kCfgSquare = 0, kCfgWide = 1, kNumCfg = 2 };
+// MFMA kernel configurations (chosen per launch: tuned, or the square one by default):
+// bit 0 is the tile shape (256 x 256 or 256 x 384), bit 1 the tail split of the launch's
+// last partial round of workgroups (tile_order.h).
+enum GemmCfg : int32_t {
+  kCfgSquare = 0,
+  kCfgWide = 1,
+  kCfgSquareSplit = 2,
+  kCfgWideSplit = 3,
+  kNumCfg = 4
+};
+constexpr int kNumShapes = 2;
+inline int cfg_shape(int cfg) { return cfg & 1; }
+inline bool cfg_split(int cfg) { return (cfg & 2) != 0; }
+constexpr int kMaxUnits = 256;   // compute units a split plans for (MI355X: 256)
+constexpr int kSplitUnit = 4;    // split pieces start and end on multiples of 4 k-steps
+constexpr int64_t kSlotFloats = int64_t(kWideM) * kWideN;  // partial sums of one tile piece
 constexpr int kKPad = 128;       // contraction dimensions are padded to this multiple
 constexpr int kEwTile = 64;      // tile edge of the momentum/transpose kernel
 constexpr int kMaxGroups = 8;    // op groups per grouped GEMM launch
@@ -92,8 +106,16 @@ struct GemmArgs {
   const float* scale;    // per matrix s = 1 / (||M'||_F + eps)
   float pa, pb, pc;
   int32_t ngroups;
-  int32_t total_tiles;
+  int32_t total_tiles;   // output tiles of the launch
+  int32_t grid;          // workgroups of the launch (total_tiles unless the tail is split)
   GroupArg g[kMaxGroups];
+  // Tail split (tile_order.h): the first dp_tiles workgroups run whole tiles (all of them
+  // when split_mode is kSplitNone), the next tail_wgs run pieces of the last tail_tiles.
+  int32_t dp_tiles;
+  int32_t split_mode, split_c, split_n;
+  int32_t tail_tiles, tail_wgs;
+  int32_t* split_cnt;    // 2 per tail tile: pieces done, partial sums written; 0 between launches
+  float* split_slots;    // kSlotFloats per piece of a tail tile
 };
 
 struct MomArgs {
@@ -111,6 +133,8 @@ struct NormArgs {
   float* scale;
   int32_t count;
   float eps;
+  int32_t* split_cnt;    // tail-split counters to clear before the contractions
+  int32_t split_cnt_n;
 };
 
 struct AdamArgs {

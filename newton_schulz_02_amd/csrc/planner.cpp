@@ -155,6 +155,15 @@ double op_flops(const PlanOp& o, int64_t m, int64_t n) {
   }
 }
 
+// K-steps of one tile of op o on matrix p: the contraction (n for the Gram formation, m for
+// every other product, none for the identity) padded to kKPad, over the elements one
+// 128-byte operand row of a stage holds.
+int op_ksteps(const PlanOp& o, const PlanMat& p) {
+  if (o.kind == kOpIdent) return 0;
+  const int64_t len = round_up(o.kind == kOpSyrk ? p.n : p.m, kKPad);
+  return int(len * int64_t(p.esize) / 128);
+}
+
 int64_t align_up(int64_t x) { return round_up(x, kAlign); }
 
 struct Span {
@@ -353,6 +362,10 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
   off = align_up(off + int64_t(count) * 4);
   plan->partial_off = off;
   off = align_up(off + mom * 4);
+  plan->split_cnt_off = off;
+  plan->split_cnt_n = 2 * kMaxUnits;
+  off = align_up(off + int64_t(plan->split_cnt_n) * 4);
+  // The partial-sum slots of the split go last, sized once the launches are known.
   for (PlanMat& p : plan->mats) {
     for (int64_t& o : p.off) o = -1;
     const int64_t es = int64_t(p.esize);
@@ -376,7 +389,7 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
       off = align_up(off + p.n * p.mp * es);
     }
   }
-  plan->ws_bytes = size_t(off);
+  int64_t ws_end = off;
 
   // Launches: momentum per dtype range, the norm, then per level and dtype the grouped GEMMs.
   std::vector<std::pair<int, int>> ranges;  // [first, last) per dtype
@@ -435,6 +448,8 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
                        [&](const G& x, const G& y) { return tile_k(x) > tile_k(y); });
       for (size_t g0 = 0; g0 < groups.size(); g0 += kMaxGroups) {
         PlanLaunch L;
+        // Per tile shape, the end of each matrix's run of tiles and its k-steps.
+        std::vector<std::pair<int64_t, int>> tile_runs[kNumShapes];
         L.kind = kLaunchGemm;
         L.dtype = plan->mats[f].dtype;
         L.level = lev;
@@ -456,14 +471,16 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
           a.tri = g.op.tri;
           a.nm = (g.op.kind == kOpUpdate && p0.tall) ? 1 : 0;  // W is n x m
           for (int i = g.first; i < g.last; ++i) L.wide_ok = L.wide_ok && plan->mats[i].wide_ok;
-          for (int cfg = 0; cfg < kNumCfg; ++cfg) {
-            a.tile_begin = int32_t(L.tiles_cfg[cfg]);
+          for (int sh = 0; sh < kNumShapes; ++sh) {
+            a.tile_begin = int32_t(L.tiles_cfg[sh]);
             for (int i = g.first; i < g.last; ++i) {
               const PlanMat& p = plan->mats[i];
-              if (cfg == kCfgSquare) L.tiles_cfg[cfg] += g.op.tri ? p.tri_tiles : p.full_tiles;
-              else L.tiles_cfg[cfg] += p.wide_tiles[g.op.tri ? 0 : (a.nm ? 2 : 1)];
+              const int64_t nt = sh == kCfgSquare ? (g.op.tri ? p.tri_tiles : p.full_tiles)
+                                                  : p.wide_tiles[g.op.tri ? 0 : (a.nm ? 2 : 1)];
+              tile_runs[sh].push_back({L.tiles_cfg[sh] + nt, op_ksteps(g.op, p)});
+              L.tiles_cfg[sh] += nt;
             }
-            L.groups_cfg[cfg].push_back(a);
+            L.groups_cfg[sh].push_back(a);
           }
           for (int i = g.first; i < g.last; ++i) L.flops += op_flops(g.op, plan->mats[i].m, plan->mats[i].n);
           sig << "|" << int(g.op.kind) << ":" << int(g.op.tri) << ":" << int(a.nm);
@@ -474,22 +491,67 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
             i = j;
           }
         }
-        for (int cfg = 0; cfg < kNumCfg; ++cfg) {
-          if (L.tiles_cfg[cfg] > INT32_MAX) {
+        for (int sh = 0; sh < kNumShapes; ++sh) {
+          if (L.tiles_cfg[sh] > INT32_MAX) {
             *err = "too many tiles in one launch";
             return MUON_EINVAL;
           }
+          // Fewest k-steps among the tiles a tail split may cut (the last kMaxUnits).
+          const int64_t from = std::max<int64_t>(0, L.tiles_cfg[sh] - kMaxUnits);
+          int64_t begin = 0;
+          int kmin = INT_MAX;
+          for (const auto& [end, ks] : tile_runs[sh]) {
+            if (end > from && end > begin) kmin = std::min(kmin, ks);
+            begin = end;
+          }
+          L.kmin_cfg[sh] = kmin == INT_MAX ? 0 : kmin;
         }
         L.signature = sig.str();
         L.cfg = choose ? (*choose)(L.signature) : kCfgSquare;
-        if (L.cfg < 0 || L.cfg >= kNumCfg || (L.cfg == kCfgWide && !L.wide_ok)) L.cfg = kCfgSquare;
-        L.groups = L.groups_cfg[L.cfg];
-        L.tiles = L.tiles_cfg[L.cfg];
         plan->launches.push_back(L);
       }
     }
   }
+  // Partial-sum slots of the tail split: enough for any unit count up to kMaxUnits (a tail
+  // of R < units tiles has at most 2 R pieces in the uneven mode and at most units, and
+  // kMaxPieces per tile, in the equal mode).
+  int64_t slots = 0;
+  for (const PlanLaunch& L : plan->launches) {
+    if (L.kind != kLaunchGemm) continue;
+    for (int sh = 0; sh < kNumShapes; ++sh) {
+      if (L.kmin_cfg[sh] / kSplitUnit < 4) continue;
+      const int64_t T = L.tiles_cfg[sh];
+      slots = std::max(slots, std::max(std::min<int64_t>(2 * T, 2 * kMaxUnits),
+                                       std::min<int64_t>(kMaxPieces * T, kMaxUnits)));
+    }
+  }
+  plan->split_slots = slots;
+  plan->split_slot_off = ws_end;
+  plan->ws_bytes = size_t(align_up(ws_end + slots * kSlotFloats * 4));
+  plan_splits(plan, kMaxUnits);
   return MUON_OK;
+}
+
+void plan_splits(Plan* plan, int units) {
+  units = std::max(1, std::min(units, kMaxUnits));
+  plan->units = units;
+  for (PlanLaunch& L : plan->launches) {
+    if (L.kind != kLaunchGemm) continue;
+    for (int sh = 0; sh < kNumShapes; ++sh)
+      L.split_cfg[sh] = plan_split(int(L.tiles_cfg[sh]), units, L.kmin_cfg[sh], kSplitUnit);
+    // The chosen configuration, where it applies: the 256 x 384 tiles only when every
+    // operand fits their 32-bit offsets, the split only when the launch has a tail to cut.
+    int cfg = L.cfg;
+    if (cfg < 0 || cfg >= kNumCfg) cfg = kCfgSquare;
+    if (cfg_shape(cfg) == kCfgWide && !L.wide_ok) cfg &= ~1;
+    if (cfg_split(cfg) && L.split_cfg[cfg_shape(cfg)].mode == kSplitNone) cfg &= ~2;
+    L.cfg = cfg;
+    const int sh = cfg_shape(cfg);
+    L.groups = L.groups_cfg[sh];
+    L.tiles = L.tiles_cfg[sh];
+    const SplitPlan& sp = L.split_cfg[sh];
+    L.grid = cfg_split(cfg) ? int64_t(sp.dp_tiles) + sp.tail_wgs : L.tiles;
+  }
 }
 
 void fill_descs(const Plan& plan, const muon_matrix* mats, const muon_hparams* hp, char* ws,
@@ -563,13 +625,30 @@ std::string describe_plan(const Plan& plan) {
   os.precision(17);
   os << "{\"count\":" << plan.mats.size() << ",\"workspace\":" << plan.ws_bytes
      << ",\"levels\":" << plan.levels << ",\"flops\":" << plan.flops
-     << ",\"bytes\":" << plan.bytes << ",\"matrices\":[";
+     << ",\"bytes\":" << plan.bytes << ",\"units\":" << plan.units
+     << ",\"desc_off\":" << plan.desc_off << ",\"scale_off\":" << plan.scale_off
+     << ",\"partial_off\":" << plan.partial_off << ",\"mom_tiles\":" << plan.total_mom_tiles
+     << ",\"split_cnt_off\":" << plan.split_cnt_off << ",\"split_cnt_n\":" << plan.split_cnt_n
+     << ",\"split_slot_off\":" << plan.split_slot_off
+     << ",\"split_slots\":" << plan.split_slots << ",\"matrices\":[";
   for (size_t i = 0; i < plan.mats.size(); ++i) {
     const PlanMat& p = plan.mats[i];
     os << (i ? "," : "") << "{\"orig\":" << p.orig << ",\"rows\":" << p.r << ",\"cols\":" << p.c
        << ",\"m\":" << p.m << ",\"n\":" << p.n << ",\"tall\":" << (p.tall ? "true" : "false")
        << ",\"dtype\":" << p.dtype << ",\"restarts\":" << p.restarts
-       << ",\"flops\":" << p.flops << ",\"ops\":[";
+       << ",\"flops\":" << p.flops << ",\"regions\":[";
+    {  // workspace byte ranges [offset, bytes] of the matrix's own buffers
+      const int64_t es = int64_t(p.esize);
+      bool first = true;
+      for (int b = 0; b < kNumBuf; ++b) {
+        if (p.off[b] < 0) continue;
+        const int64_t bytes = b < kSlot0 + kSlots ? p.m * p.mp * es
+                              : (b == kXrIn || b == kXrWs) ? p.m * p.np * es : p.n * p.mp * es;
+        os << (first ? "" : ",") << "[" << p.off[b] << "," << bytes << "]";
+        first = false;
+      }
+    }
+    os << "],\"ops\":[";
     for (size_t j = 0; j < p.ops.size(); ++j) {
       const PlanOp& o = p.ops[j];
       os << (j ? "," : "") << "{\"kind\":\"" << kKind[int(o.kind)] << "\",\"level\":" << o.level
@@ -585,7 +664,17 @@ std::string describe_plan(const Plan& plan) {
     const PlanLaunch& L = plan.launches[i];
     os << (i ? "," : "") << "{\"kind\":\"" << kLaunch[L.kind] << "\",\"dtype\":" << L.dtype
        << ",\"level\":" << L.level << ",\"tiles\":" << L.tiles << ",\"cfg\":" << L.cfg
+       << ",\"grid\":" << L.grid
        << ",\"tiles_cfg\":[" << L.tiles_cfg[0] << "," << L.tiles_cfg[1] << "]"
+       << ",\"kmin_cfg\":[" << L.kmin_cfg[0] << "," << L.kmin_cfg[1] << "]"
+       << ",\"split_cfg\":[";
+    for (int sh = 0; sh < kNumShapes; ++sh) {
+      const SplitPlan& sp = L.split_cfg[sh];
+      os << (sh ? "," : "") << "{\"mode\":" << sp.mode << ",\"c\":" << sp.c << ",\"n\":" << sp.n
+         << ",\"dp_tiles\":" << sp.dp_tiles << ",\"tail\":" << sp.tail
+         << ",\"tail_wgs\":" << sp.tail_wgs << ",\"slots\":" << sp.slots << "}";
+    }
+    os << "]"
        << ",\"wide_ok\":" << (L.wide_ok ? "true" : "false")
        << ",\"signature\":\"" << L.signature << "\",\"flops\":" << L.flops
        << ",\"groups\":[";

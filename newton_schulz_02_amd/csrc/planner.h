@@ -9,6 +9,7 @@
 
 #include "../../include/muon.h"
 #include "muon_internal.h"
+#include "tile_order.h"
 
 namespace muon {
 
@@ -50,9 +51,12 @@ struct PlanLaunch {
   int first = 0, last = 0;       // momentum: matrix range
   std::vector<GroupArg> groups;  // gemm: the groups of the chosen kernel configuration
   int64_t tiles = 0;
-  int cfg = kCfgSquare;          // gemm: the chosen MFMA kernel configuration
-  std::vector<GroupArg> groups_cfg[kNumCfg];  // gemm: the groups under each configuration
-  int64_t tiles_cfg[kNumCfg] = {0, 0};
+  int cfg = kCfgSquare;          // gemm: the chosen MFMA kernel configuration (GemmCfg)
+  int64_t grid = 0;              // gemm: workgroups of the chosen configuration
+  std::vector<GroupArg> groups_cfg[kNumShapes];  // gemm: the groups under each tile shape
+  int64_t tiles_cfg[kNumShapes] = {0, 0};
+  int kmin_cfg[kNumShapes] = {0, 0};   // gemm: fewest k-steps among the last kMaxUnits tiles
+  SplitPlan split_cfg[kNumShapes];     // gemm: tail split under each tile shape
   bool wide_ok = true;           // gemm: the 256 x 384 configuration may run this launch
   std::string signature;         // gemm: shapes and ops of the launch (the tuning key)
   double flops = 0, bytes = 0;
@@ -62,6 +66,11 @@ struct Plan {
   std::vector<PlanMat> mats;     // sorted order
   std::vector<PlanLaunch> launches;
   int64_t desc_off = 0, scale_off = 0, partial_off = 0;
+  // Tail split: 2 counters per tail tile and one partial-sum slot per piece.
+  int64_t split_cnt_off = 0, split_slot_off = 0;
+  int32_t split_cnt_n = 0;
+  int64_t split_slots = 0;
+  int units = kMaxUnits;         // compute units the splits are planned for
   int64_t total_mom_tiles = 0;
   size_t ws_bytes = 0;
   int levels = 0;
@@ -76,6 +85,11 @@ using CfgChooser = std::function<int(const std::string& signature)>;
 // chooser every launch uses the square-tile kernel.
 int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, Plan* plan,
                std::string* err, const CfgChooser* choose = nullptr);
+
+// Plan the tail split of every MFMA launch for `units` compute units (capped at
+// kMaxUnits) and apply the chosen configurations' grids.  build_plan calls it with
+// kMaxUnits; a device with fewer units re-plans before launching.
+void plan_splits(Plan* plan, int units);
 
 // Fill the device descriptor table for a concrete workspace base address.
 void fill_descs(const Plan& plan, const muon_matrix* mats, const muon_hparams* hp, char* ws,

@@ -128,4 +128,119 @@ MUON_HD void full_band_decode(int t, int TM, int TN, int& ti, int& tj) {
   ti = kBand * s + u % h;
 }
 
+// ---- tail split -----------------------------------------------------------------------
+// A launch of T tiles on P compute units (one workgroup per unit at a time) runs F = T / P
+// whole rounds; the R = T - F P tiles left over would hold R units for a whole tile time
+// while the other P - R wait.  With the tail split the first F P workgroups run whole tiles
+// as usual and the R tail tiles are cut along the contraction into pieces, one workgroup
+// per piece:
+//   kSplitEqual  (R <= P / 2): every tail tile is cut into c equal pieces (c R workgroups,
+//                the c pieces of a tile and neighbouring tiles on one XCD); the tail takes
+//                about 1/c of a tile time.
+//   kSplitUneven (R > P / 2):  every tail tile is cut once, at s = K n / (n + 1) with
+//                n = ceil(R / (P - R)).  Each XCD takes a run of tail tiles and gets the
+//                workgroups of their first pieces [0, s) before those of their second pieces
+//                [s, K): its units start on the long first pieces, and the rest run about n
+//                second pieces each, so the tail takes about n / (n + 1) of a tile time.
+// Pieces start and end on multiples of `unit` k-steps (the kernels' stage counts divide
+// it), so each piece runs whole blocks of stages.  The last piece of a tile to finish adds
+// the others' partial sums, in piece order, and stores the tile.
+enum SplitMode : int32_t { kSplitNone = 0, kSplitEqual = 1, kSplitUneven = 2 };
+constexpr int kMaxPieces = 8;
+
+// The piece run by tail workgroup j (j in [0, wgs), in launch order; workgroup j runs on
+// XCD j mod kXcds).  Returns false for a workgroup with no piece (padding of the uneven
+// mode's deal); else tail tile t, piece `piece` of `pieces`.
+MUON_HD bool split_item(int mode, int R, int wgs, int c, int j, int& t, int& piece, int& pieces) {
+  t = 0;
+  piece = 0;
+  pieces = 1;
+  if (mode == kSplitEqual) {
+    const int u = xcd_remap(j, wgs);
+    pieces = c;
+    t = u / c;
+    piece = u % c;
+    return t < R;
+  }
+  if (mode != kSplitUneven) return false;
+  // wgs is a multiple of 2 kXcds: XCD x runs wgs / kXcds workgroups, the first pieces of
+  // tail tiles [x m, x m + m) and then their second pieces, m = wgs / (2 kXcds).
+  const int m = wgs / (2 * kXcds);
+  const int x = j % kXcds, i = j / kXcds;
+  pieces = 2;
+  piece = i < m ? 0 : 1;
+  t = x * m + (i < m ? i : i - m);
+  return t < R;
+}
+
+// K-step range [k0, k1) of piece `piece` of `pieces` of a tile of K k-steps.  Cuts fall on
+// multiples of unit; the last piece ends at K (which need not be one).  n is the uneven
+// mode's second pieces per unit.
+MUON_HD void split_range(int mode, int n, int K, int unit, int piece, int pieces, int& k0, int& k1) {
+  const int u = K / unit;
+  if (mode == kSplitEqual) {
+    k0 = unit * (piece * u / pieces);
+    k1 = piece == pieces - 1 ? K : unit * ((piece + 1) * u / pieces);
+    return;
+  }
+  if (mode == kSplitUneven) {
+    int s = (u * n + (n + 1) / 2) / (n + 1);
+    if (s > u - 1) s = u - 1;
+    if (s < 1) s = 1;
+    if (s > u) s = u;
+    k0 = piece == 0 ? 0 : unit * s;
+    k1 = piece == 0 ? unit * s : K;
+    return;
+  }
+  k0 = 0;
+  k1 = K;
+}
+
+// Split of a launch of T tiles over P units: mode, pieces per tail tile (equal mode) or
+// second pieces per workgroup (uneven mode), the workgroups of the whole tiles and of the
+// tail.  kmin is the smallest k-step count of the tail tiles; no piece is made shorter
+// than two units.
+struct SplitPlan {
+  int mode = kSplitNone;
+  int c = 1;          // equal mode: pieces per tail tile
+  int n = 1;          // uneven mode: second pieces per unit (sets the cut)
+  int dp_tiles = 0;   // whole tiles, run first
+  int tail = 0;       // tail tiles R
+  int tail_wgs = 0;   // workgroups of the tail pieces
+  int slots = 0;      // partial-sum slots (one per piece of a tail tile)
+};
+
+MUON_HD SplitPlan plan_split(int T, int P, int kmin, int unit) {
+  SplitPlan s;
+  s.dp_tiles = T;
+  if (T <= 0 || P <= 1) return s;
+  const int R = T % P;
+  const int units = kmin / unit;
+  if (R == 0 || units < 4) return s;
+  if (2 * R <= P) {
+    int c = P / R;
+    if (c > kMaxPieces) c = kMaxPieces;
+    if (c > units / 2) c = units / 2;
+    if (c < 2) return s;
+    s.mode = kSplitEqual;
+    s.c = c;
+    s.tail_wgs = c * R;
+    s.slots = c * R;
+  } else {
+    const int n = (R + (P - R) - 1) / (P - R);
+    int k0, k1;
+    split_range(kSplitUneven, n, kmin, unit, 0, 2, k0, k1);
+    const int first = k1, second = n * (kmin - k1);
+    // Worth it only if the longer side of the tail is clearly shorter than a whole tile.
+    if (10 * (first > second ? first : second) > 9 * kmin) return s;
+    s.mode = kSplitUneven;
+    s.n = n;
+    s.tail_wgs = (2 * R + 2 * kXcds - 1) / (2 * kXcds) * (2 * kXcds);
+    s.slots = 2 * R;
+  }
+  s.dp_tiles = T - R;
+  s.tail = R;
+  return s;
+}
+
 }  // namespace muon

@@ -90,7 +90,7 @@ def test_tile_counts_of_both_configurations(shapes):
         assert dtype == "bf16"
         assert sum(c for *_, c in groups) >= 1
         assert tuple(L["tiles_cfg"]) == _expected_tiles(groups), L["signature"]
-        assert L["cfg"] == 0 and L["tiles"] == L["tiles_cfg"][0]
+        assert L["cfg"] == 0 and L["tiles"] == L["tiles_cfg"][0] and L["grid"] == L["tiles"]
 
 
 def test_nm_flag_marks_the_transposed_tall_update():
@@ -133,7 +133,7 @@ def test_table_and_force_select_the_configuration(clean_table):
     assert nm.tune_table() == {sig: 1}
     for s, c, tiles, tcfg in _cfgs(shapes):
         assert c == (1 if s == sig else 0)
-        assert tiles == tcfg[c]
+        assert tiles == tcfg[c & 1]
     nm.tune_force(nm.CFG_WIDE)
     assert all(c == 1 for _, c, _, _ in _cfgs(shapes))
     nm.tune_force(nm.CFG_SQUARE)
@@ -157,7 +157,7 @@ def test_export_import_round_trip(clean_table):
     assert nm.tune_table()["bf16|0:1:0:640x640*1"] == 0
 
 
-@pytest.mark.parametrize("bad", ["sig", "sig 2", "sig -1", " 1", "a b 1", "sig 1x", "sig "])
+@pytest.mark.parametrize("bad", ["sig", "sig 4", "sig -1", " 1", "a b 1", "sig 1x", "sig ", "sig 12"])
 def test_malformed_import_adds_nothing(clean_table, bad):
     nm.tune_import("keep 1\n")
     with pytest.raises(nm.MuonError):
@@ -166,7 +166,7 @@ def test_malformed_import_adds_nothing(clean_table, bad):
 
 
 def test_argument_errors(clean_table):
-    for cfg in (-2, 2, 7):
+    for cfg in (-2, 4, 7):
         with pytest.raises(nm.MuonError):
             nm.tune_force(cfg)
     hp = nm.make_hparams()
