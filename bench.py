@@ -48,26 +48,33 @@ def kernel_hash(kernel: str = "gemm_bf16") -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel: str, workload: str, launches: list[int]):
+def traffic_from_profiles(kernel: str, workload: str, launches: list[tuple[int, int]]):
     """HBM bytes per launch of an MFMA kernel, from the committed counter summary.
 
-    The summary lists, per kernel, the bytes of each MFMA launch of the workload's plan (in
-    plan order) and the kernel's source hash.  ``launches`` are the plan indices the kernel
-    ran; the result is the mean of their bytes.  A hash that differs from the sources' means
-    the kernel changed since the counters were taken: the figure is withheld (None).
+    The summary lists, per kernel configuration c (0..3), the bytes of each MFMA launch of the
+    workload's plan (in plan order) when it runs under c (``launch_bytes cfg<c>``), and the
+    source hash of each kernel.  ``launches`` holds (plan index, configuration) of the
+    launches the kernel ran; the result is the mean of their bytes.  A hash that differs from
+    the sources' means the kernel changed since the counters were taken: the figure is
+    withheld (None).
     """
     path = ROOT / "profiles" / f"gemm_{workload}_hbm_traffic.md"
     if not path.exists() or not launches:
         return None
     text = path.read_text()
     m_hash = re.search(rf"^kernel_hash {kernel}:\s*([0-9a-f]+)", text, re.M)
-    m_bytes = re.search(rf"^launch_bytes {kernel}:\s*([0-9.eE+, ]+)$", text, re.M)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash(kernel):
+    if not m_hash or m_hash.group(1) != kernel_hash(kernel):
         return None
-    per_launch = [float(x) for x in m_bytes.group(1).split(",")]
-    if max(launches) >= len(per_launch):
-        return None
-    return sum(per_launch[i] for i in launches) / len(launches)
+    total = 0.0
+    for i, cfg in launches:
+        m_bytes = re.search(rf"^launch_bytes cfg{cfg}:\s*([0-9.eE+, ]+)$", text, re.M)
+        if not m_bytes:
+            return None
+        per_launch = [float(x) for x in m_bytes.group(1).split(",")]
+        if i >= len(per_launch):
+            return None
+        total += per_launch[i]
+    return total / len(launches)
 
 
 def cpu_baseline(wl, budget_s: float = 30.0):
@@ -230,7 +237,7 @@ def main() -> int:
     achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
     wide_dominant = gemm_name.startswith("gemm_wide")
     traffic = traffic_from_profiles(gemm_name, wl.name,
-                                    [i for i, c in enumerate(cfg_of_launch) if bool(c & 1) == wide_dominant])
+                                    [(i, c) for i, c in enumerate(cfg_of_launch) if bool(c & 1) == wide_dominant])
     kernels = {k: {"launches": v["launches"] // args.steps, "ms_per_step": v["ms"] / args.steps,
                    "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None,
                    "gbs": (v["bytes"] / (v["ms"] * 1e-3) / 1e9) if v["bytes"] else None}
