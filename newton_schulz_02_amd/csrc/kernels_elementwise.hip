@@ -61,6 +61,16 @@ __device__ __forceinline__ void store_chunk(S* p, const Chunk<S>& c) {
   *(g_u32x4)(p) = *reinterpret_cast<const u32x4*>(c.v);
 }
 
+// A chunk's values widened to fp32 (8 bf16 -> two 16-byte stores); p is 16-byte aligned.
+template <typename S>
+__device__ __forceinline__ void store_f32(float* p, const Chunk<S>& c) {
+  float f[Chunk<S>::N];
+#pragma unroll
+  for (int e = 0; e < Chunk<S>::N; ++e) f[e] = as_f(c.v[e]);
+#pragma unroll
+  for (int q = 0; q < Chunk<S>::N / 4; ++q) *(g_u32x4)(p + 4 * q) = *reinterpret_cast<const u32x4*>(f + 4 * q);
+}
+
 template <typename S>
 __global__ __launch_bounds__(256) void k_momentum(MomArgs a) {
   constexpr int CH = 16 / sizeof(S);  // elements per 16-byte chunk
@@ -125,8 +135,12 @@ __global__ __launch_bounds__(256) void k_momentum(MomArgs a) {
       ss = fmaf(x, x, ss);
       tile[li][lc + e] = x;
     }
-    // Same-orientation zero-padded copy: rows < r, columns < round_up(c, 64).
-    if (copy && gi < r) store_chunk(copy + int64_t(gi) * d.copy_ld + gj, out);
+    // Same-orientation zero-padded copy: rows < r, columns < round_up(c, 64); fp32 for a bf16
+    // matrix whose Gram iteration runs in fp32.
+    if (copy && gi < r) {
+      if (sizeof(S) == 2 && d.gram_f32) store_f32(static_cast<float*>(d.copy_out) + int64_t(gi) * d.copy_ld + gj, out);
+      else store_chunk(copy + int64_t(gi) * d.copy_ld + gj, out);
+    }
   }
 
   // Transposed copy: row j (< c) holds column j of M'; columns < round_up(r, 64).
@@ -141,7 +155,10 @@ __global__ __launch_bounds__(256) void k_momentum(MomArgs a) {
         Chunk<S> o;
 #pragma unroll
         for (int e = 0; e < CH; ++e) st_f(&o.v[e], tile[lc + e][lj]);
-        store_chunk(trans + int64_t(gj) * d.trans_ld + i0 + lc, o);
+        if (sizeof(S) == 2 && d.gram_f32)
+          store_f32(static_cast<float*>(d.trans_out) + int64_t(gj) * d.trans_ld + i0 + lc, o);
+        else
+          store_chunk(trans + int64_t(gj) * d.trans_ld + i0 + lc, o);
       }
     }
   }

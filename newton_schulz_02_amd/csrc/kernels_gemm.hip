@@ -528,23 +528,30 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
     }
     if (kind == kOpUpdate) {  // W -= eta * alpha * (A B^T)
       const float step = d.eta * alpha;
-      for (int idx = tid; idx < kChunksHalf; idx += kThreads) {
-        const int rr = idx / kRowChunks, cc = (idx % kRowChunks) * 8;
-        const int gi = hr0 + rr, gj = col0 + cc;
-        if (gi >= rows_out || gj >= cols_out) continue;
-        const gptr<S> p = Cp + int64_t(gi) * ldc + gj;
-        if (d.wvec && gj + 7 < cols_out) {
-          Vec8<S> w;
-          load8<S>(p, w);
+      // W's element type Wt: S, or bf16 for a bf16 matrix whose Gram iteration ran in fp32.
+      auto update = [&](auto wt) {
+        using Wt = decltype(wt);
+        const gptr<Wt> Wp = to_global(static_cast<Wt*>(C.ptr));
+        for (int idx = tid; idx < kChunksHalf; idx += kThreads) {
+          const int rr = idx / kRowChunks, cc = (idx % kRowChunks) * 8;
+          const int gi = hr0 + rr, gj = col0 + cc;
+          if (gi >= rows_out || gj >= cols_out) continue;
+          const gptr<Wt> p = Wp + int64_t(gi) * ldc + gj;
+          if (d.wvec && gj + 7 < cols_out) {
+            Vec8<Wt> w;
+            load8<Wt>(p, w);
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            w.v[e] = from_f(fmaf(-step, ep_at(rr, cc + e), to_f(w.v[e])), static_cast<S*>(nullptr));
-          store8(p, w);
-        } else {
-          for (int e = 0; e < 8 && gj + e < cols_out; ++e)
-            p[e] = from_f(fmaf(-step, ep_at(rr, cc + e), to_f(p[e])), static_cast<S*>(nullptr));
+            for (int e = 0; e < 8; ++e)
+              w.v[e] = from_f(fmaf(-step, ep_at(rr, cc + e), to_f(w.v[e])), static_cast<Wt*>(nullptr));
+            store8(p, w);
+          } else {
+            for (int e = 0; e < 8 && gj + e < cols_out; ++e)
+              p[e] = from_f(fmaf(-step, ep_at(rr, cc + e), to_f(p[e])), static_cast<Wt*>(nullptr));
+          }
         }
-      }
+      };
+      if (sizeof(S) == 4 && d.gram_f32) update(uint16_t());
+      else update(S());
     } else if (g.tri) {
       for (int idx = tid; idx < kChunksHalf; idx += kThreads) {
         const int rr = idx / kRowChunks, cc = (idx % kRowChunks) * 8;

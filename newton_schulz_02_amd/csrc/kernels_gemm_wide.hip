@@ -201,6 +201,7 @@ struct EpArgs {
   gptr<const S> E;
   int64_t ldc, ldt, lde;
   int rows_out, cols_out, m, d_rows, d_cols, t_rows, t_cols, wvec;
+  int wbf16;    // the update's W is bf16 (a bf16 matrix whose Gram iteration ran in fp32)
   int r0, c0;   // first row and column of the wave's block
   int lane;
 };
@@ -289,18 +290,24 @@ __device__ __attribute__((always_inline)) inline void ep_wave(f32x16 (&acc)[kFra
       const int gi = sr0 + r, gj = e.c0 + c8;
       if constexpr (K == kOpUpdate) {  // W -= eta * alpha * (A B^T)
         if (gi >= e.rows_out || gj >= e.cols_out) continue;
-        const gptr<S> pw = e.C + int64_t(gi) * e.ldc + gj;
-        if (e.wvec && gj + 7 < e.cols_out) {
-          Vec8<S> w;
-          load8<S>(pw, w);
+        // W's element type Wt: S, or bf16 for a bf16 matrix whose Gram iteration ran in fp32.
+        auto update = [&](auto wt) {
+          using Wt = decltype(wt);
+          const gptr<Wt> pw = (gptr<Wt>)(e.C) + int64_t(gi) * e.ldc + gj;
+          if (e.wvec && gj + 7 < e.cols_out) {
+            Vec8<Wt> w;
+            load8<Wt>(pw, w);
 #pragma unroll
-          for (int q = 0; q < 8; ++q)
-            w.v[q] = from_f(fmaf(-e.step, slab[(c8 + q) * ld + r], to_f(w.v[q])), static_cast<S*>(nullptr));
-          store8(pw, w);
-        } else {
-          for (int q = 0; q < 8 && gj + q < e.cols_out; ++q)
-            pw[q] = from_f(fmaf(-e.step, slab[(c8 + q) * ld + r], to_f(pw[q])), static_cast<S*>(nullptr));
-        }
+            for (int q = 0; q < 8; ++q)
+              w.v[q] = from_f(fmaf(-e.step, slab[(c8 + q) * ld + r], to_f(w.v[q])), static_cast<Wt*>(nullptr));
+            store8(pw, w);
+          } else {
+            for (int q = 0; q < 8 && gj + q < e.cols_out; ++q)
+              pw[q] = from_f(fmaf(-e.step, slab[(c8 + q) * ld + r], to_f(pw[q])), static_cast<Wt*>(nullptr));
+          }
+        };
+        if (sizeof(S) == 4 && e.wbf16) update(uint16_t());
+        else update(S());
       } else {
         if (gi >= e.d_rows || gj >= e.d_cols) continue;
         if (sym && gi < gj) continue;  // chunk above the diagonal
@@ -524,6 +531,7 @@ __device__ __forceinline__ void gemm_wide_tile(const GemmArgs& args, const int b
   e.t_rows = xform ? d.buf[g.c2].rows : rows_out;
   e.t_cols = xform ? d.buf[g.c2].kpad : C.kpad;
   e.wvec = d.wvec;
+  e.wbf16 = d.gram_f32;
   e.r0 = row0 + kWaveRows * wm;
   e.c0 = col0 + kWaveCols * wn;
   e.lane = lane;

@@ -82,6 +82,8 @@ struct MatDesc {
   int64_t trans_ld;
   int32_t rows, cols;
   int32_t vec;           // rows of G and M are 16-byte aligned: vector access allowed
+  int32_t gram_f32;      // bf16 matrix iterating in fp32: its X copies and Gram slots are fp32,
+                         // and the (fp32 kernel's) update rounds W to bf16
   int32_t wvec;          // rows of W are 16-byte aligned: vector access allowed
   int32_t mom_prefix;    // first momentum tile of this matrix (all matrices, sorted order)
   int32_t mom_tiles_c;   // momentum tiles along cols (cover round_up(cols, kKPad))

@@ -161,10 +161,17 @@ double op_flops(const PlanOp& o, int64_t m, int64_t n) {
 int op_ksteps(const PlanOp& o, const PlanMat& p) {
   if (o.kind == kOpIdent) return 0;
   const int64_t len = round_up(o.kind == kOpSyrk ? p.n : p.m, kKPad);
-  return int(len * int64_t(p.esize) / 128);
+  return int(len * int64_t(p.gsize) / 128);
 }
 
 int64_t align_up(int64_t x) { return round_up(x, kAlign); }
+
+}  // namespace
+
+// Gram dtype (see planner.h).
+int gram_dtype(int dtype, int64_t m) { return (dtype == kBF16 && m <= kF32GramMaxM) ? int(kF32) : dtype; }
+
+namespace {
 
 struct Span {
   uintptr_t lo, hi;
@@ -292,9 +299,12 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
     p.np = round_up(p.n, kKPad);
     p.dtype = x.dtype;
     p.esize = x.dtype == MUON_BF16 ? 2 : 4;
+    p.gdtype = gram_dtype(p.dtype, p.m);
+    p.gsize = p.gdtype == kBF16 ? 2 : 4;
     p.restarts = resolve_restarts(hp->restart_mask, p.m, p.n, steps);
   }
   std::stable_sort(plan->mats.begin(), plan->mats.end(), [](const PlanMat& a, const PlanMat& b) {
+    if (a.gdtype != b.gdtype) return a.gdtype < b.gdtype;
     if (a.dtype != b.dtype) return a.dtype < b.dtype;
     if (a.restarts != b.restarts) return a.restarts < b.restarts;
     if (a.tall != b.tall) return a.tall < b.tall;
@@ -324,7 +334,7 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
     p.wide_tiles[2] = ceil_div(p.n, kWideM) * ceil_div(p.m, kWideN);
     {  // largest operand, with a tile's overhang of rows, below 2^31 bytes
       const int64_t big = std::max(p.m, p.n);
-      p.wide_ok = (big + kWideN) * round_up(big, kKPad) * int64_t(p.esize) < (int64_t(1) << 31);
+      p.wide_ok = (big + kWideN) * round_up(big, kKPad) * int64_t(p.gsize) < (int64_t(1) << 31);
     }
     // Momentum tiles cover the extents rounded up to kKPad, so that the zero padding of the
     // row and transposed copies (leading dimensions rounded to kKPad) is written too.
@@ -368,7 +378,7 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
   // The partial-sum slots of the split go last, sized once the launches are known.
   for (PlanMat& p : plan->mats) {
     for (int64_t& o : p.off) o = -1;
-    const int64_t es = int64_t(p.esize);
+    const int64_t es = int64_t(p.gsize);  // Gram iterates and X forms hold the Gram dtype
     for (int s = 0; s < kSlots; ++s) {
       p.off[kSlot0 + s] = off;
       off = align_up(off + p.m * p.mp * es);
@@ -391,15 +401,21 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
   }
   int64_t ws_end = off;
 
-  // Launches: momentum per dtype range, the norm, then per level and dtype the grouped GEMMs.
-  std::vector<std::pair<int, int>> ranges;  // [first, last) per dtype
-  for (int i = 0; i < count;) {
-    int j = i;
-    while (j < count && plan->mats[j].dtype == plan->mats[i].dtype) ++j;
-    ranges.push_back({i, j});
-    i = j;
-  }
-  for (auto [f, l] : ranges) {
+  // Launches: momentum per run of one input dtype, the norm, then per level and Gram dtype
+  // the grouped GEMMs (the sort keeps both kinds of run contiguous).
+  auto runs = [&](auto key) {
+    std::vector<std::pair<int, int>> out;  // [first, last)
+    for (int i = 0; i < count;) {
+      int j = i;
+      while (j < count && key(plan->mats[j]) == key(plan->mats[i])) ++j;
+      out.push_back({i, j});
+      i = j;
+    }
+    return out;
+  };
+  const auto mom_ranges = runs([](const PlanMat& p) { return p.dtype; });
+  const auto ranges = runs([](const PlanMat& p) { return p.gdtype; });
+  for (auto [f, l] : mom_ranges) {
     PlanLaunch L;
     L.kind = kLaunchMomentum;
     L.dtype = plan->mats[f].dtype;
@@ -451,7 +467,7 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
         // Per tile shape, the end of each matrix's run of tiles and its k-steps.
         std::vector<std::pair<int64_t, int>> tile_runs[kNumShapes];
         L.kind = kLaunchGemm;
-        L.dtype = plan->mats[f].dtype;
+        L.dtype = plan->mats[f].gdtype;
         L.level = lev;
         std::ostringstream sig;
         sig << (L.dtype == kBF16 ? "bf16" : "f32");
@@ -573,7 +589,10 @@ void fill_descs(const Plan& plan, const muon_matrix* mats, const muon_hparams* h
                 ? 1
                 : 0;
     d.wvec = ((uintptr_t)x.param % 16 == 0 && (p.c * es) % 16 == 0) ? 1 : 0;
-    const bool caller_ok = (p.c % kKPad == 0) && ((uintptr_t)x.momentum % 16 == 0);
+    // The caller's momentum can serve as a form of X when it has the Gram dtype, a 128-multiple
+    // leading dimension and 16-byte alignment.
+    const bool caller_ok = p.gdtype == p.dtype && (p.c % kKPad == 0) && ((uintptr_t)x.momentum % 16 == 0);
+    d.gram_f32 = (p.gdtype == kF32 && p.dtype == kBF16) ? 1 : 0;
     for (int s = 0; s < kSlots; ++s)
       d.buf[kSlot0 + s] = {at(kSlot0 + s), p.mp, int32_t(p.m), int32_t(p.mp)};
     const BufDesc row_ws = {at(kXrIn), p.np, int32_t(p.m), int32_t(p.np)};
@@ -635,10 +654,10 @@ std::string describe_plan(const Plan& plan) {
     const PlanMat& p = plan.mats[i];
     os << (i ? "," : "") << "{\"orig\":" << p.orig << ",\"rows\":" << p.r << ",\"cols\":" << p.c
        << ",\"m\":" << p.m << ",\"n\":" << p.n << ",\"tall\":" << (p.tall ? "true" : "false")
-       << ",\"dtype\":" << p.dtype << ",\"restarts\":" << p.restarts
+       << ",\"dtype\":" << p.dtype << ",\"gram_dtype\":" << p.gdtype << ",\"restarts\":" << p.restarts
        << ",\"flops\":" << p.flops << ",\"regions\":[";
     {  // workspace byte ranges [offset, bytes] of the matrix's own buffers
-      const int64_t es = int64_t(p.esize);
+      const int64_t es = int64_t(p.gsize);
       bool first = true;
       for (int b = 0; b < kNumBuf; ++b) {
         if (p.off[b] < 0) continue;

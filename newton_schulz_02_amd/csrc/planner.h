@@ -26,8 +26,10 @@ struct PlanMat {
   int orig = 0;                  // index in the caller's list
   int64_t r = 0, c = 0, m = 0, n = 0, mp = 0, np = 0;
   bool tall = false;
-  int dtype = kBF16;
+  int dtype = kBF16;              // the caller's buffers (G, M, W)
   size_t esize = 2;
+  int gdtype = kBF16;             // the Gram iterates, X forms and contractions (gram_dtype)
+  size_t gsize = 2;
   uint32_t restarts = 0;
   std::vector<PlanOp> ops;
   int64_t off[kNumBuf];          // workspace offsets of workspace-resident buffers, -1 if none
@@ -94,6 +96,16 @@ void plan_splits(Plan* plan, int units);
 // Fill the device descriptor table for a concrete workspace base address.
 void fill_descs(const Plan& plan, const muon_matrix* mats, const muon_hparams* hp, char* ws,
                 std::vector<MatDesc>* out);
+
+// Dtype of a matrix's Gram iteration: bf16 matrices with m <= kF32GramMaxM iterate in fp32.
+// With few Gram rows each bf16 product sums few terms, so the rounding of the stored iterates
+// does not average out; measured on thin bf16 matrices (m <= 48, n up to 8192) it took the
+// result past the 2e-2 bar (up to 7e-2 at m = 4), while m >= 64 stayed near 1e-2.  The fp32
+// products of such small Gram spaces cost little next to the bf16 contractions over n.  Their
+// Gram formation and update then run in the fp32 kernel on fp32 copies of X, and the update
+// rounds W back to bf16.
+constexpr int64_t kF32GramMaxM = 128;
+int gram_dtype(int dtype, int64_t m);
 
 // Resolve the restart set of one matrix (bit k = re-anchor before iteration k).
 uint32_t resolve_restarts(uint32_t mask, int64_t m, int64_t n, int steps);

@@ -222,7 +222,7 @@ def test_buckets_are_contiguous_and_sorted():
 
 
 def test_mixed_dtypes_get_separate_launches():
-    arr = nm.shape_array([(64, 128, nm.MUON_BF16), (64, 128, nm.MUON_F32)])
+    arr = nm.shape_array([(200, 300, nm.MUON_BF16), (64, 128, nm.MUON_F32)])
     p = nm.plan_describe(arr, 2, HP)
     moms = [L for L in p["launches"] if L["kind"] == "momentum"]
     assert sorted(L["dtype"] for L in moms) == [1, 2]
@@ -230,6 +230,30 @@ def test_mixed_dtypes_get_separate_launches():
         if L["kind"] == "gemm":
             dt = {p["matrices"][i]["dtype"] for g in L["groups"] for i in range(g["first"], g["last"])}
             assert dt == {L["dtype"]}
+
+
+@pytest.mark.parametrize("m", [1, 4, 33, 64, 128, 129, 256])
+def test_small_bf16_matrices_iterate_in_fp32(m):
+    """bf16 matrices with at most 128 Gram rows run their Gram iteration in fp32: they share
+    the fp32 contraction launches (a launch's dtype is its operands'), while their momentum
+    launch stays bf16; their workspace forms are fp32."""
+    arr = nm.shape_array([(m, 4 * m + 100, nm.MUON_BF16), (300, 700, nm.MUON_BF16),
+                          (50, 90, nm.MUON_F32)])
+    p = nm.plan_describe(arr, 3, HP)
+    small = next(x for x in p["matrices"] if x["orig"] == 0)
+    assert small["dtype"] == 1 and small["gram_dtype"] == (2 if m <= 128 else 1)
+    assert next(x for x in p["matrices"] if x["orig"] == 1)["gram_dtype"] == 1
+    assert next(x for x in p["matrices"] if x["orig"] == 2)["gram_dtype"] == 2
+    moms = [L for L in p["launches"] if L["kind"] == "momentum"]
+    assert sorted(L["dtype"] for L in moms) == [1, 2]
+    for L in p["launches"]:
+        if L["kind"] == "gemm":
+            gd = {p["matrices"][i]["gram_dtype"] for g in L["groups"] for i in range(g["first"], g["last"])}
+            assert gd == {L["dtype"]}
+    # Gram slots of the small matrix hold fp32: m x round_up(m, 128) x 4 bytes.
+    es = 4 if m <= 128 else 2
+    mp = -(-m // 128) * 128
+    assert small["regions"][0][1] == m * mp * es
 
 
 def test_workspace_size_independent_of_pointers_and_grows_with_count():

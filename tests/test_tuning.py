@@ -87,19 +87,26 @@ def test_tile_counts_of_both_configurations(shapes):
     assert gemms
     for L in gemms:
         dtype, groups = _signature_groups(L["signature"])
-        assert dtype == "bf16"
+        # The signature names the launch's operand dtype: bf16, or f32 for the Gram iteration
+        # of bf16 matrices with at most 128 Gram rows.
+        assert dtype == {1: "bf16", 2: "f32"}[L["dtype"]]
+        assert all((m <= 128) == (dtype == "f32") for *_, m, n, c in groups)
         assert sum(c for *_, c in groups) >= 1
         assert tuple(L["tiles_cfg"]) == _expected_tiles(groups), L["signature"]
         assert L["cfg"] == 0 and L["tiles"] == L["tiles_cfg"][0] and L["grid"] == L["tiles"]
 
 
 def test_nm_flag_marks_the_transposed_tall_update():
+    d = nm.plan_describe(nm.shape_array([(300, 200)]), 1, nm.make_hparams())
+    last = [L for L in d["launches"] if L["kind"] == "gemm"][-1]
+    assert last["signature"] == "bf16|4:0:1:200x300*1"
+    d = nm.plan_describe(nm.shape_array([(200, 300)]), 1, nm.make_hparams())
+    last = [L for L in d["launches"] if L["kind"] == "gemm"][-1]
+    assert last["signature"] == "bf16|4:0:0:200x300*1"
+    # A small bf16 matrix iterates (and updates) in the fp32 kernel.
     d = nm.plan_describe(nm.shape_array([(300, 100)]), 1, nm.make_hparams())
     last = [L for L in d["launches"] if L["kind"] == "gemm"][-1]
-    assert last["signature"] == "bf16|4:0:1:100x300*1"
-    d = nm.plan_describe(nm.shape_array([(100, 300)]), 1, nm.make_hparams())
-    last = [L for L in d["launches"] if L["kind"] == "gemm"][-1]
-    assert last["signature"] == "bf16|4:0:0:100x300*1"
+    assert last["signature"] == "f32|4:0:1:100x300*1"
 
 
 def test_fp32_signatures_name_their_dtype():
