@@ -1,4 +1,4 @@
-"""CPU float64 oracle for the owner-side Muon step (test infrastructure only).
+"""CPU float64 oracles for the owner-side Muon and Shampoo steps (test infrastructure only).
 
 Importable only from ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py``; the product package never imports it.
@@ -16,4 +16,11 @@ from .ns_oracle import (  # noqa: F401
     orient,
     orthogonalize,
     update_scale,
+)
+from .shampoo_oracle import (  # noqa: F401
+    accumulate,
+    inverse_root_eigh,
+    inverse_root_newton,
+    root_scale,
+    shampoo_step,
 )
