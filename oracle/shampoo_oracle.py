@@ -39,7 +39,7 @@ def accumulate(S: np.ndarray, X: np.ndarray, beta2: float) -> np.ndarray:
 
 def root_scale(S: np.ndarray, eps: float) -> float:
     """nu = ||S||_F + eps: an upper bound on the largest eigenvalue of S + eps I."""
-    return float(np.linalg.norm(np.asarray(S, dtype=np.float64))) + eps
+    return float(np.linalg.norm(np.asarray(S, dtype=np.float64))) + float(eps)
 
 
 def inverse_root_newton(A: np.ndarray, nu: float, iters: int, p: int = 4) -> np.ndarray:
@@ -50,6 +50,7 @@ def inverse_root_newton(A: np.ndarray, nu: float, iters: int, p: int = 4) -> np.
     X_k tends to A^(-1/p) and M_k to I when the eigenvalues of A / nu lie in (0, 1].
     """
     A = np.asarray(A, dtype=np.float64)
+    nu = float(nu)
     n = A.shape[0]
     eye = np.eye(n)
     X = nu ** (-1.0 / p) * eye
@@ -71,6 +72,9 @@ def inverse_root_eigh(A: np.ndarray, p: int = 4) -> np.ndarray:
 def shampoo_step(W, G, L, R, *, lr: float, beta2: float = 1.0, eps: float = 1e-6, iters: int = 20):
     """One owner-side Shampoo step on a matrix W (r x c) with gradient G and statistics L
     (r x r), R (c x c).  Returns (W', L', R') in float64."""
+    # Hyperparameters as Python floats: a float32 scalar must not pull the float64 arithmetic
+    # down to float32 (numpy keeps the scalar's precision in mixed scalar expressions).
+    lr, beta2, eps = float(lr), float(beta2), float(eps)
     W = np.asarray(W, dtype=np.float64)
     G = np.asarray(G, dtype=np.float64)
     L1 = accumulate(L, G, beta2)
