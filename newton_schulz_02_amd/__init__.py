@@ -7,7 +7,8 @@ has not been built, every call raises ``MuonLibraryMissing``; there is no fallba
 Entry points mirror ``include/muon.h``: :func:`workspace_size`, :func:`muon_step`,
 :func:`adamw_step`, :func:`step_cost`, :func:`plan_describe`, :func:`profile_begin`,
 :func:`profile_end`, :func:`strerror`, :func:`last_error`, :func:`version`,
-:func:`shutdown`.
+:func:`shutdown`; and ``include/shampoo.h``: :func:`shampoo_workspace_size`,
+:func:`shampoo_step` (:class:`ShampooStep`), :func:`shampoo_plan_describe`.
 """
 
 from __future__ import annotations
@@ -65,8 +66,20 @@ class muon_kernel_stat(ctypes.Structure):
                 ("flops", c_double), ("bytes", c_double)]
 
 
+class shampoo_matrix(ctypes.Structure):
+    _fields_ = [("param", c_void_p), ("grad", c_void_p), ("stat_left", c_void_p),
+                ("stat_right", c_void_p), ("rows", c_int64), ("cols", c_int64), ("dtype", c_int32),
+                ("reserved", c_int32)]
+
+
+class shampoo_hparams(ctypes.Structure):
+    _fields_ = [("lr", c_float), ("beta2", c_float), ("eps", c_float), ("root_iters", c_int32)]
+
+
 _MATP = POINTER(muon_matrix)
 _HPP = POINTER(muon_hparams)
+_SMATP = POINTER(shampoo_matrix)
+_SHPP = POINTER(shampoo_hparams)
 _SIGNATURES = {
     "muon_workspace_size": (c_int, [_MATP, c_int32, _HPP, POINTER(c_size_t)]),
     "muon_step": (c_int, [_MATP, c_int32, _HPP, c_void_p, c_size_t, c_void_p]),
@@ -90,6 +103,9 @@ _SIGNATURES = {
     "muon_tune_import": (c_int, [c_char_p]),
     "muon_debug_wide_tile_order": (c_int, [c_int, c_int, c_int, POINTER(c_int), POINTER(c_int)]),
     "muon_debug_split": (c_int, [c_int, c_int, c_int, POINTER(c_int), POINTER(c_int), c_int]),
+    "shampoo_workspace_size": (c_int, [_SMATP, c_int32, _SHPP, POINTER(c_size_t)]),
+    "shampoo_step": (c_int, [_SMATP, c_int32, _SHPP, c_void_p, c_size_t, c_void_p]),
+    "shampoo_plan_describe": (c_int, [_SMATP, c_int32, _SHPP, c_char_p, c_size_t]),
 }
 
 _lib = None
@@ -377,3 +393,97 @@ def profile_end() -> dict:
     return {out[i].name.decode(): {"launches": out[i].launches, "ms": out[i].ms,
                                    "flops": out[i].flops, "bytes": out[i].bytes}
             for i in range(min(n.value, 16))}
+
+
+# --- Shampoo (include/shampoo.h) --------------------------------------------------------
+
+def make_shampoo_hparams(lr=0.01, beta2=1.0, eps=1e-6, root_iters=20) -> shampoo_hparams:
+    return shampoo_hparams(float(lr), float(beta2), float(eps), int(root_iters))
+
+
+def shampoo_matrix_array(params, grads, lefts, rights):
+    """Pack lists of fp32 device tensors into a ctypes shampoo_matrix array: param and grad
+    rows x cols, left statistic rows x rows, right statistic cols x cols."""
+    import torch
+
+    if not (len(params) == len(grads) == len(lefts) == len(rights)):
+        raise ValueError("params, grads, lefts and rights must have the same length")
+    arr = (shampoo_matrix * max(1, len(params)))()
+    for i, (w, g, lt, rt) in enumerate(zip(params, grads, lefts, rights)):
+        r, c = (w.shape[0], w.shape[1]) if w.dim() == 2 else (0, 0)
+        want = {"param": (w, (r, c)), "grad": (g, (r, c)), "left": (lt, (r, r)), "right": (rt, (c, c))}
+        for name, (t, shape) in want.items():
+            if t.dim() != 2 or not t.is_contiguous() or tuple(t.shape) != shape:
+                raise ValueError(f"matrix {i}: {name} must be a contiguous {shape[0]} x {shape[1]} tensor")
+            if t.dtype != torch.float32:
+                raise TypeError(f"matrix {i}: {name} must be float32")
+        arr[i] = shampoo_matrix(w.data_ptr(), g.data_ptr(), lt.data_ptr(), rt.data_ptr(), r, c, MUON_F32, 0)
+    return arr
+
+
+def shampoo_shape_array(shapes):
+    """A shampoo_matrix array with fake, distinct, aligned pointers: for host-only planning calls."""
+    arr = (shampoo_matrix * max(1, len(shapes)))()
+    base = 1 << 40
+    page = lambda n: ((n * 4 + 4095) // 4096) * 4096  # noqa: E731
+    for i, (r, c) in enumerate(shapes):
+        w, g, lt, rt = base, base + page(r * c), base + 2 * page(r * c), base + 2 * page(r * c) + page(r * r)
+        arr[i] = shampoo_matrix(w, g, lt, rt, r, c, MUON_F32, 0)
+        base = rt + page(c * c)
+    return arr
+
+
+def shampoo_workspace_size_raw(arr, count: int, hp: shampoo_hparams) -> int:
+    out = c_size_t(0)
+    _check(lib().shampoo_workspace_size(arr, int(count), ctypes.byref(hp), ctypes.byref(out)))
+    return int(out.value)
+
+
+def shampoo_step_raw(arr, count: int, hp: shampoo_hparams, ws_ptr: int, ws_bytes: int, stream_ptr) -> None:
+    _check(lib().shampoo_step(arr, int(count), ctypes.byref(hp), c_void_p(ws_ptr), int(ws_bytes),
+                              stream_ptr))
+
+
+def shampoo_plan_describe(arr, count: int, hp: shampoo_hparams, size: int = 1 << 24) -> dict:
+    buf = ctypes.create_string_buffer(size)
+    _check(lib().shampoo_plan_describe(arr, int(count), ctypes.byref(hp), buf, size))
+    return json.loads(buf.value.decode())
+
+
+def shampoo_workspace_size(params, grads, lefts, rights, **hp) -> int:
+    return shampoo_workspace_size_raw(shampoo_matrix_array(params, grads, lefts, rights), len(params),
+                                      make_shampoo_hparams(**hp))
+
+
+class ShampooStep:
+    """A prepared Shampoo step over fixed lists of fp32 device tensors (params and both
+    statistics updated in place by each call)."""
+
+    def __init__(self, params, grads, lefts, rights, *, lr=0.01, beta2=1.0, eps=1e-6, root_iters=20,
+                 workspace=None):
+        import torch
+
+        self.params, self.grads = list(params), list(grads)
+        self.lefts, self.rights = list(lefts), list(rights)
+        self.count = len(self.params)
+        self.hp = make_shampoo_hparams(lr, beta2, eps, root_iters)
+        self.arr = shampoo_matrix_array(self.params, self.grads, self.lefts, self.rights)
+        self.ws_bytes = shampoo_workspace_size_raw(self.arr, self.count, self.hp)
+        self.device = self.params[0].device if self.count else torch.device("cuda")
+        if workspace is None:
+            workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
+        if workspace.numel() < self.ws_bytes:
+            raise ValueError(f"workspace has {workspace.numel()} bytes, needs {self.ws_bytes}")
+        self.workspace = workspace
+
+    def plan(self) -> dict:
+        return shampoo_plan_describe(self.arr, self.count, self.hp)
+
+    def __call__(self, stream=None) -> None:
+        shampoo_step_raw(self.arr, self.count, self.hp, self.workspace.data_ptr(), self.workspace.numel(),
+                         _stream_handle(stream, self.device))
+
+
+def shampoo_step(params, grads, lefts, rights, *, stream=None, **hp) -> None:
+    """One Shampoo step over lists of fp32 device tensors."""
+    ShampooStep(params, grads, lefts, rights, **hp)(stream)

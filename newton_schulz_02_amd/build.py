@@ -23,7 +23,7 @@ BUILD = PKG / "_build"
 LIB = PKG / "libmuon.so"
 ARCH = "gfx950"
 
-SOURCES = ["planner.cpp", "muon_api.cpp", "owner.cpp", "kernels_elementwise.hip", "kernels_gemm.hip",
+SOURCES = ["planner.cpp", "shampoo_plan.cpp", "muon_api.cpp", "owner.cpp", "kernels_elementwise.hip", "kernels_gemm.hip",
            "kernels_gemm_wide.hip"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

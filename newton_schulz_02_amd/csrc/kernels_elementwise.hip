@@ -107,7 +107,17 @@ __global__ __launch_bounds__(256) void k_momentum(MomArgs a) {
     Chunk<S> out;
     if (gi < r) {
       const int64_t base = int64_t(gi) * c + gj;
-      if (d.vec && gj + CH <= c) {
+      if (!M) {  // no momentum buffer: M' = G, only the copies and sums are written
+        if (d.vec && gj + CH <= c) {
+          load_chunk(G + base, out);
+        } else {
+#pragma unroll
+          for (int e = 0; e < CH; ++e) {
+            if (gj + e < c) out.v[e] = G[base + e];
+            else st_f(&out.v[e], 0.0f);
+          }
+        }
+      } else if (d.vec && gj + CH <= c) {
         Chunk<S> gv, mv;
         load_chunk(G + base, gv);
         load_chunk(M + base, mv);

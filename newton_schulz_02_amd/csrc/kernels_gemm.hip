@@ -194,6 +194,7 @@ __device__ __forceinline__ float tri_value(int kind, int gi, int gj, int m, floa
   if (kind == kOpSyrk) return alpha * x;
   if (kind == kOpPoly) return (gi == gj ? pa : 0.0f) + pb * to_f(E[int64_t(er) * lde + ec]) + pc * x;
   if (kind == kOpIdent) return gi == gj ? 1.0f : 0.0f;
+  if (kind == kOpAffine) return alpha * ((gi == gj ? pa : 0.0f) + pb * to_f(E[int64_t(er) * lde + ec]));
   return x;
 }
 
@@ -235,7 +236,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
 
   const BufDesc C = d.buf[g.c];
   const int kind = g.kind;
-  const bool ident = kind == kOpIdent;
+  const bool ident = kind == kOpIdent || kind == kOpAffine;  // no contraction
   const BufDesc A = ident ? C : d.buf[g.a];
   const BufDesc B = ident ? C : d.buf[g.b];
   const int rows_out = A.rows;
@@ -373,6 +374,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
   float alpha = 1.0f;
   if (g.alpha == kAlphaS) alpha = args.scale[lo];
   else if (g.alpha == kAlphaS2) alpha = args.scale[lo] * args.scale[lo];
+  else if (g.alpha == kAlphaQuarter) alpha = sqrtf(sqrtf(args.scale[lo]));
   const gptr<S> Cp = to_global(static_cast<S*>(C.ptr));
   const int64_t ldc = C.ld;
   const gptr<const S> E = to_global(static_cast<const S*>(g.e >= 0 ? d.buf[g.e].ptr : C.ptr));
@@ -401,7 +403,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
           // The polynomial's iterate: E[gj][gi0 .. gi0+3] = E[gi0 .. gi0+3][gj], 8 bytes per
           // (j, r4); all 8 loads of this i are issued before any is used.
           u32x2 e4[kFragN][4];
-          if constexpr (K == kOpPoly) {
+          if constexpr (K == kOpPoly || K == kOpAffine) {
 #pragma unroll
             for (int j = 0; j < kFragN; ++j)
 #pragma unroll
@@ -435,6 +437,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
                                    pb * to_f(reinterpret_cast<const uint16_t*>(&e4[j][r4])[q]) + pc * x
                              : 0.0f;
                   else if constexpr (K == kOpIdent) val = (in && gi == gj) ? 1.0f : 0.0f;
+                  else if constexpr (K == kOpAffine)
+                    val = in ? alpha * ((gi == gj ? pa : 0.0f) +
+                                        pb * to_f(reinterpret_cast<const uint16_t*>(&e4[j][r4])[q]))
+                             : 0.0f;
                   else val = in ? x : 0.0f;
                 }
                 o[q] = from_f(val, static_cast<uint16_t*>(nullptr));
@@ -449,16 +455,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
           case kOpPoly: stage(std::integral_constant<int, kOpPoly>{}); break;
           case kOpXform: stage(std::integral_constant<int, kOpXform>{}); break;
           case kOpIdent: stage(std::integral_constant<int, kOpIdent>{}); break;
+          case kOpAffine: stage(std::integral_constant<int, kOpAffine>{}); break;
           default: stage(std::integral_constant<int, kOpProd>{}); break;
         }
       }
       __syncthreads();
-      // Transposed-side pass: row gj = col0 + c of the output gets tile rows r .. r+7.
-      const gptr<S> Tp = xform ? to_global(static_cast<S*>(d.buf[g.c2].ptr)) : Cp;
-      const int64_t ldt = xform ? d.buf[g.c2].ld : ldc;
-      const int t_rows = xform ? d.buf[g.c2].rows : m;          // valid output rows
-      const int t_cols = xform ? d.buf[g.c2].kpad : cstore;     // stored output columns
-      for (int idx = tid; idx < kTile * 32; idx += kThreads) {
+      // Transposed-side pass: row gj = col0 + c of the output gets tile rows r .. r+7 (an
+      // xform without a transposed output skips it).
+      const bool tpass = !xform || g.c2 >= 0;
+      const BufDesc T2 = (xform && g.c2 >= 0) ? d.buf[g.c2] : C;
+      const gptr<S> Tp = xform ? to_global(static_cast<S*>(T2.ptr)) : Cp;
+      const int64_t ldt = xform ? T2.ld : ldc;
+      const int t_rows = xform ? T2.rows : m;          // valid output rows
+      const int t_cols = xform ? T2.kpad : cstore;     // stored output columns
+      for (int idx = tid; tpass && idx < kTile * 32; idx += kThreads) {
         const int c = idx / 32, r = (idx % 32) * 8;
         const int gj = col0 + c, gi = row0 + r;
         if (gj >= t_rows || gi >= t_cols) continue;
@@ -559,7 +569,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
         if (gi >= m || gi < gj) continue;  // row invalid, or the chunk lies above the diagonal
         if (gi >= gj + 7 && gj + 7 < m) {
           Vec8<S> e8, out;
-          if (kind == kOpPoly) load8<S>(E + int64_t(gi) * lde + gj, e8);
+          if (kind == kOpPoly || kind == kOpAffine) load8<S>(E + int64_t(gi) * lde + gj, e8);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float x = ident ? 0.0f : ep_at(rr, cc + e);
@@ -567,6 +577,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
             if (kind == kOpSyrk) val = alpha * x;
             else if (kind == kOpPoly) val = (gi == gj + e ? pa : 0.0f) + pb * to_f(e8.v[e]) + pc * x;
             else if (kind == kOpIdent) val = gi == gj + e ? 1.0f : 0.0f;
+            else if (kind == kOpAffine) val = alpha * ((gi == gj + e ? pa : 0.0f) + pb * to_f(e8.v[e]));
             else val = x;
             out.v[e] = from_f(val, static_cast<S*>(nullptr));
           }
@@ -587,7 +598,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
         if (gj >= m || gi + 7 <= gj) continue;  // row of C invalid, or chunk on/above diagonal
         if (gi > gj && gi + 7 < m) {
           Vec8<S> e8, out;
-          if (kind == kOpPoly) load8<S>(E + int64_t(gj) * lde + gi, e8);
+          if (kind == kOpPoly || kind == kOpAffine) load8<S>(E + int64_t(gj) * lde + gi, e8);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float x = ident ? 0.0f : ep_at(rr + e, cc);
@@ -595,6 +606,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
             if (kind == kOpSyrk) val = alpha * x;
             else if (kind == kOpPoly) val = pb * to_f(e8.v[e]) + pc * x;  // off-diagonal: no pa
             else if (kind == kOpIdent) val = 0.0f;
+            else if (kind == kOpAffine) val = alpha * pb * to_f(e8.v[e]);
             else val = x;
             out.v[e] = from_f(val, static_cast<S*>(nullptr));
           }
@@ -613,7 +625,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
       // Row form C (rows < C.rows, columns < C.kpad, zero beyond cols_out) and its
       // transpose C2 (rows < C2.rows, columns < C2.kpad, zero beyond rows_out).  Both
       // leading dimensions are multiples of 8, so chunks never straddle the padding edge.
-      const BufDesc C2 = d.buf[g.c2];
+      const BufDesc C2 = g.c2 >= 0 ? d.buf[g.c2] : C;
       const gptr<S> C2p = to_global(static_cast<S*>(C2.ptr));
       for (int idx = tid; idx < kChunksHalf; idx += kThreads) {
         const int rr = idx / kRowChunks, cc = (idx % kRowChunks) * 8;
@@ -625,7 +637,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
           out.v[e] = from_f(gj + e < cols_out ? alpha * ep_at(rr, cc + e) : 0.0f, static_cast<S*>(nullptr));
         store8(Cp + int64_t(gi) * ldc + gj, out);
       }
-      for (int idx = tid; idx < kChunksHalf; idx += kThreads) {
+      for (int idx = tid; g.c2 >= 0 && idx < kChunksHalf; idx += kThreads) {
         const int rr = (idx % kColChunks) * 8, cc = idx / kColChunks;
         const int gi = hr0 + rr, gj = col0 + cc;
         if (gj >= C2.rows || gi >= C2.kpad) continue;

@@ -512,6 +512,7 @@ __device__ __forceinline__ void gemm_wide_tile(const GemmArgs& args, const int b
   e.alpha = 1.0f;
   if (g.alpha == kAlphaS) e.alpha = args.scale[lo];
   else if (g.alpha == kAlphaS2) e.alpha = args.scale[lo] * args.scale[lo];
+  else if (g.alpha == kAlphaQuarter) e.alpha = sqrtf(sqrtf(args.scale[lo]));
   e.pa = args.pa;
   e.pb = args.pb;
   e.pc = args.pc;

@@ -15,6 +15,7 @@
 #include "../../include/muon.h"
 #include "muon_internal.h"
 #include "planner.h"
+#include "shampoo_plan.h"
 
 using namespace muon;
 
@@ -197,9 +198,9 @@ int run_launch(int dev, hipStream_t s, const Plan& plan, const PlanLaunch& L, in
   std::memset(&a, 0, sizeof a);
   a.desc = ddesc;
   a.scale = scale;
-  a.pa = hp->ns_a;
-  a.pb = hp->ns_b;
-  a.pc = hp->ns_c;
+  a.pa = L.own_coef ? L.pa : hp->ns_a;
+  a.pb = L.own_coef ? L.pb : hp->ns_b;
+  a.pc = L.own_coef ? L.pc : hp->ns_c;
   const int shape = cfg_shape(cfg);
   const std::vector<GroupArg>& groups = L.groups_cfg[shape];
   a.ngroups = int32_t(groups.size());
@@ -454,6 +455,107 @@ int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, vo
     return MUON_OK;
   } catch (const std::exception& ex) {
     return fail(MUON_EHIP, std::string("exception: ") + ex.what());
+  }
+}
+
+int shampoo_workspace_size(const shampoo_matrix* mats, int32_t count, const shampoo_hparams* hp,
+                           size_t* bytes) {
+  try {
+    if (!bytes) return fail(MUON_EINVAL, "bytes is NULL");
+    ShampooPlan sp;
+    std::string err;
+    const int rc = build_shampoo_plan(mats, count, hp, &sp, &err);
+    if (rc != MUON_OK) return fail(rc, err);
+    *bytes = count > 0 ? sp.plan.ws_bytes : 0;
+    return MUON_OK;
+  } catch (const std::exception& e) {
+    return fail(MUON_EINVAL, e.what());
+  }
+}
+
+int shampoo_plan_describe(const shampoo_matrix* mats, int32_t count, const shampoo_hparams* hp,
+                          char* buf, size_t len) {
+  try {
+    if (!buf || len == 0) return fail(MUON_EINVAL, "buf is NULL or empty");
+    ShampooPlan sp;
+    std::string err;
+    const int rc = build_shampoo_plan(mats, count, hp, &sp, &err);
+    if (rc != MUON_OK) return fail(rc, err);
+    const std::string s = describe_shampoo_plan(sp);
+    const size_t n = std::min(len - 1, s.size());
+    std::memcpy(buf, s.data(), n);
+    buf[n] = '\0';
+    if (s.size() >= len) return fail(MUON_ENOSPC, "description truncated");
+    return MUON_OK;
+  } catch (const std::exception& e) {
+    return fail(MUON_EINVAL, e.what());
+  }
+}
+
+int shampoo_step(const shampoo_matrix* mats, int32_t count, const shampoo_hparams* hp,
+                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+  try {
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    std::lock_guard<std::mutex> lock(g_mu);
+    ShampooPlan sp;
+    std::string err;
+    int rc = build_shampoo_plan(mats, count, hp, &sp, &err);
+    if (rc != MUON_OK) return fail(rc, err);
+    if (count == 0) return MUON_OK;
+    if (!workspace) return fail(MUON_EINVAL, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(MUON_EINVAL, "workspace is not 256-byte aligned");
+    if (workspace_bytes < sp.plan.ws_bytes) {
+      char buf[128];
+      snprintf(buf, sizeof buf, "workspace has %zu bytes, needs %zu", workspace_bytes, sp.plan.ws_bytes);
+      return fail(MUON_ENOSPC, buf);
+    }
+    char* ws = static_cast<char*>(workspace);
+    std::vector<MatDesc> descs;
+    fill_shampoo_descs(sp, mats, hp, ws, &descs);
+    int dev = 0;
+    if ((rc = current_device(&dev)) != MUON_OK) return rc;
+    if ((rc = check_device(dev)) != MUON_OK) return rc;
+    rc = upload(dev, descs.data(), descs.size() * sizeof(MatDesc), ws + sp.plan.desc_off, s);
+    if (rc != MUON_OK) return rc;
+    // The launches read only eps (the norm) and beta (unused: no momentum buffer) from here.
+    muon_hparams h;
+    std::memset(&h, 0, sizeof h);
+    h.lr = hp->lr;
+    h.eps = hp->eps;
+    const int entries = int(descs.size());
+    for (const PlanLaunch& L : sp.plan.launches) {
+      if (L.kind == kLaunchCopyIn || L.kind == kLaunchCopyOut) {
+        const bool in = L.kind == kLaunchCopyIn;
+        double bytes = 0.0;
+        for (int e = L.first; e < L.last; ++e) {
+          const double m = double(sp.plan.mats[size_t(e)].m);
+          bytes += 8.0 * m * m;
+        }
+        rc = timed(dev, s, "copy_stat", 0.0, bytes, [&]() -> int {
+          for (int e = L.first; e < L.last; ++e) {
+            const PlanMat& p = sp.plan.mats[size_t(e)];
+            const int j = e - count;
+            const shampoo_matrix& x = mats[sp.stat_mat[size_t(j)]];
+            char* state = static_cast<char*>(sp.stat_right[size_t(j)] ? x.stat_right : x.stat_left);
+            char* slot = ws + p.off[sp.stat_slot];
+            const size_t row = size_t(p.m) * 4, pitch = size_t(p.mp) * 4;
+            const hipError_t e2 = in ? hipMemcpy2DAsync(slot, pitch, state, row, row, size_t(p.m),
+                                                        hipMemcpyDeviceToDevice, s)
+                                     : hipMemcpy2DAsync(state, row, slot, pitch, row, size_t(p.m),
+                                                        hipMemcpyDeviceToDevice, s);
+            if (e2 != hipSuccess) return int(e2);
+          }
+          return int(hipSuccess);
+        });
+      } else {
+        rc = run_launch(dev, s, sp.plan, L, L.cfg, ws, &h, entries);
+      }
+      if (rc != MUON_OK) return rc;
+    }
+    return MUON_OK;
+  } catch (const std::exception& e) {
+    return fail(MUON_EHIP, std::string("exception: ") + e.what());
   }
 }
 

@@ -60,10 +60,12 @@ enum OpKind : int8_t {
   kOpProd = 2,    // C = A B^T, lower tiles, mirrored
   kOpXform = 3,   // C = alpha * A B^T (full tiles) and C2 = its transpose
   kOpUpdate = 4,  // W -= eta * alpha * A B^T (full tiles)
-  kOpIdent = 5    // C = I (lower tiles, mirrored; no contraction)
+  kOpIdent = 5,   // C = I (lower tiles, mirrored; no contraction)
+  kOpAffine = 6   // C = alpha * (pa*I + pb*E) (lower tiles, mirrored; no contraction)
 };
 
-enum AlphaMode : int8_t { kAlphaOne = 0, kAlphaS = 1, kAlphaS2 = 2 };
+// alpha of an op: 1, the matrix's scale s, s^2, or s^(1/4).
+enum AlphaMode : int8_t { kAlphaOne = 0, kAlphaS = 1, kAlphaS2 = 2, kAlphaQuarter = 3 };
 
 struct BufDesc {
   void* ptr;
@@ -75,7 +77,7 @@ struct BufDesc {
 struct MatDesc {
   BufDesc buf[kNumBuf];
   const void* grad;      // caller G (rows x cols)
-  void* mom;             // caller M (rows x cols), updated in place
+  void* mom;             // caller M (rows x cols), updated in place; null: M' = G, nothing stored
   void* copy_out;        // padded same-orientation copy of M' (rows x round_up(cols,kKPad)) or null
   void* trans_out;       // transposed copy of M' (cols x round_up(rows,kKPad)) or null
   int64_t copy_ld;
@@ -99,7 +101,7 @@ struct MatDesc {
 struct GroupArg {
   int32_t first, last;   // matrix range [first, last) in the descriptor table
   int32_t tile_begin;    // first launch tile of this group
-  int8_t kind, a, b, c, c2, e, alpha, tri;
+  int8_t kind, a, b, c, c2, e, alpha, tri;  // c2 < 0: an xform stores no transposed copy
   int8_t nm;             // full output of n x m elements (the update of a tall matrix)
 };
 

@@ -639,7 +639,7 @@ void fill_descs(const Plan& plan, const muon_matrix* mats, const muon_hparams* h
 }
 
 std::string describe_plan(const Plan& plan) {
-  static const char* kKind[] = {"syrk", "poly", "prod", "xform", "update", "ident"};
+  static const char* kKind[] = {"syrk", "poly", "prod", "xform", "update", "ident", "affine"};
   std::ostringstream os;
   os.precision(17);
   os << "{\"count\":" << plan.mats.size() << ",\"workspace\":" << plan.ws_bytes
@@ -678,7 +678,7 @@ std::string describe_plan(const Plan& plan) {
     os << "]}";
   }
   os << "],\"launches\":[";
-  static const char* kLaunch[] = {"momentum", "norm", "gemm"};
+  static const char* kLaunch[] = {"momentum", "norm", "gemm", "copy_in", "copy_out"};
   for (size_t i = 0; i < plan.launches.size(); ++i) {
     const PlanLaunch& L = plan.launches[i];
     os << (i ? "," : "") << "{\"kind\":\"" << kLaunch[L.kind] << "\",\"dtype\":" << L.dtype

@@ -44,7 +44,15 @@ struct PlanMat {
   double flops = 0, bytes = 0;
 };
 
-enum LaunchKind { kLaunchMomentum = 0, kLaunchNorm = 1, kLaunchGemm = 2 };
+// kLaunchCopyIn / kLaunchCopyOut (Shampoo): copy the caller's statistics of entries
+// [first, last) into their workspace slot, and back.
+enum LaunchKind {
+  kLaunchMomentum = 0,
+  kLaunchNorm = 1,
+  kLaunchGemm = 2,
+  kLaunchCopyIn = 3,
+  kLaunchCopyOut = 4
+};
 
 struct PlanLaunch {
   int kind = kLaunchGemm;
@@ -60,6 +68,8 @@ struct PlanLaunch {
   int kmin_cfg[kNumShapes] = {0, 0};   // gemm: fewest k-steps among the last kMaxUnits tiles
   SplitPlan split_cfg[kNumShapes];     // gemm: tail split under each tile shape
   bool wide_ok = true;           // gemm: the 256 x 384 configuration may run this launch
+  bool own_coef = false;         // gemm: pa, pb, pc below (else the Newton-Schulz a, b, c)
+  float pa = 0.0f, pb = 0.0f, pc = 0.0f;
   std::string signature;         // gemm: shapes and ops of the launch (the tuning key)
   double flops = 0, bytes = 0;
 };

@@ -208,3 +208,44 @@ def generate_tail(wl: Workload, device=None):
     if device is not None:
         p, g, m, v = p.to(device), g.to(device), m.to(device), v.to(device)
     return p, g, m, v
+
+
+# --- Shampoo inputs ----------------------------------------------------------------------
+
+def _spd(rng: np.random.Generator, n: int, scale: float, cond: float) -> np.ndarray:
+    """Q diag(lam) Q^T: Q Haar-orthogonal (QR of a Gaussian, column signs fixed by R's
+    diagonal), lam log-uniform over [scale / cond, scale], in float64."""
+    Q, R = np.linalg.qr(rng.standard_normal((n, n)))
+    Q = Q * np.sign(np.where(np.diag(R) == 0, 1.0, np.diag(R)))
+    lam = scale * np.exp(rng.uniform(-np.log(cond), 0.0, n))
+    S = (Q * lam) @ Q.T
+    return (S + S.T) / 2
+
+
+def shampoo_inputs(shapes, seed: int, *, grad_std: float = 1e-2, weight_std: float = 0.02,
+                   stats: str = "warm", cond: float = 1e3):
+    """Yield (W, G, L0, R0) per (rows, cols) shape as float32 CPU tensors.
+
+    Recipe: ``numpy.random.Generator(PCG64(seed))``; per matrix in list order draw W0 and G
+    as float32 normals times weight_std and grad_std, then (``stats="warm"``) the left and
+    the right statistic as symmetric positive definite matrices Q diag(lam) Q^T with lam
+    log-uniform over [s / cond, s], s = grad_std^2 max(rows, cols) (the size of the
+    eigenvalues of one G G^T), rounded to float32 and made exactly symmetric; or zero
+    statistics (``stats="zero"``, a first step).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    for r, c in shapes:
+        W = _draw(rng, (r, c), weight_std, F32)
+        G = _draw(rng, (r, c), grad_std, F32)
+        if stats == "warm":
+            s = grad_std ** 2 * max(r, c)
+            Lm = _spd(rng, r, s, cond).astype(np.float32)
+            Rm = _spd(rng, c, s, cond).astype(np.float32)
+            L0 = torch.from_numpy(np.triu(Lm) + np.triu(Lm, 1).T)
+            R0 = torch.from_numpy(np.triu(Rm) + np.triu(Rm, 1).T)
+        elif stats == "zero":
+            L0 = torch.zeros((r, r), dtype=torch.float32)
+            R0 = torch.zeros((c, c), dtype=torch.float32)
+        else:
+            raise ValueError(f"stats must be 'warm' or 'zero', not {stats!r}")
+        yield W, G, L0, R0

@@ -1,0 +1,141 @@
+"""Parity of the owner-side Shampoo step (HIP path, through the C ABI) with the float64 oracle.
+
+Tolerances, from the arithmetic: the statistics are one fp32 accumulation (relative error
+near 1e-7 times a small factor of the sum length), bound here at 1e-5; the update X_L G X_R
+goes through 4 (K - 1) fp32 products per root, and a float32 run of the same iteration on
+the CPU stays below 2.5e-5 relative Frobenius error on these inputs (statistics with
+condition number <= 1e3 after regularisation), so the fp32 bar of 1e-4 holds with margin.
+Statistics whose regularised condition number approaches 1 / (fp32 epsilon) are outside that
+bar (the eigenvalues below it are not resolved in fp32); the zero-statistics cases therefore
+use an eps of 1e-2 of the gradient's eigenvalue scale.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import newton_schulz_02_amd as nm
+from newton_schulz_02_amd import workloads as W
+from oracle import shampoo_step as oracle_step
+
+from tests.gpu_helpers import DEV, log, relf, to64
+
+pytestmark = pytest.mark.gpu
+
+STAT_TOL = 1e-5
+UPD_TOL = 1e-4
+
+
+def _run(shapes, seed, *, stats="warm", iters=5, beta2=0.9, eps=None, lr=0.05, steps=1, grad_std=1e-2):
+    """Run `steps` Shampoo steps on the GPU (a fresh gradient each step after the first) and the
+    oracle on the same inputs; return the worst relative errors (update, statistics)."""
+    log(f"shampoo shapes={shapes} seed={seed} stats={stats} iters={iters} beta2={beta2} steps={steps}")
+    items = list(W.shampoo_inputs(shapes, seed, stats=stats, grad_std=grad_std))
+    if eps is None:
+        eps = 1e-2 * grad_std ** 2 * max(max(s) for s in shapes) if stats == "zero" else 1e-6
+    Ws = [w.to(DEV) for w, _, _, _ in items]
+    Gs = [g.to(DEV) for _, g, _, _ in items]
+    Ls = [lt.to(DEV) for _, _, lt, _ in items]
+    Rs = [rt.to(DEV) for _, _, _, rt in items]
+    ref = [[to64(t) for t in x] for x in items]  # W, G, L, R per matrix
+    step = nm.ShampooStep(Ws, Gs, Ls, Rs, lr=lr, beta2=beta2, eps=eps, root_iters=iters)
+    rng = np.random.default_rng(seed + 1000)
+    upd, stat = 0.0, 0.0
+    for k in range(steps):
+        if k > 0:  # new gradients, written in place so the prepared step sees them
+            for i, g in enumerate(Gs):
+                new = torch.from_numpy((rng.standard_normal(tuple(g.shape)) * grad_std).astype(np.float32))
+                g.copy_(new)
+                ref[i][1] = new.double().numpy()
+        W_before = [to64(w) for w in Ws]
+        step()
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            w0, g0, l0, r0 = ref[i]
+            w1, l1, r1 = oracle_step(w0, g0, l0, r0, lr=lr, beta2=np.float32(beta2), eps=np.float32(eps),
+                                     iters=iters)
+            gw, gl, gr = to64(Ws[i]), to64(Ls[i]), to64(Rs[i])
+            stat = max(stat, relf(gl, l1), relf(gr, r1))
+            upd = max(upd, relf(gw - W_before[i], w1 - w0))
+            # the next step starts from the GPU's state (the statistics and W it wrote)
+            ref[i] = [gw, g0, gl, gr]
+    log(f"  update {upd:.3e}  statistics {stat:.3e}")
+    return upd, stat
+
+
+SHAPES = [
+    [(64, 64)],
+    [(300, 200)],
+    [(200, 300)],
+    [(129, 513)],
+    [(513, 129)],
+    [(512, 512)],
+    [(1, 300)],
+    [(300, 1)],
+    [(1, 1)],
+    [(257, 255)],
+]
+
+
+@pytest.mark.parametrize("shapes", SHAPES, ids=lambda s: "x".join(map(str, s[0])))
+def test_single_matrix(shapes):
+    upd, stat = _run(shapes, seed=sum(shapes[0]), iters=8)
+    assert stat <= STAT_TOL
+    assert upd <= UPD_TOL
+
+
+@pytest.mark.parametrize("iters", [1, 2, 3, 20])
+def test_iteration_counts(iters):
+    upd, stat = _run([(200, 300), (96, 96)], seed=11 + iters, iters=iters)
+    assert stat <= STAT_TOL and upd <= UPD_TOL
+
+
+@pytest.mark.parametrize("beta2", [0.0, 0.5, 1.0])
+def test_beta2(beta2):
+    upd, stat = _run([(150, 260)], seed=21, beta2=beta2, iters=6)
+    assert stat <= STAT_TOL and upd <= UPD_TOL
+
+
+def test_mixed_list_shares_launches():
+    shapes = [(64, 64), (200, 300), (513, 129), (1, 7), (384, 384), (33, 700)]
+    upd, stat = _run(shapes, seed=31, iters=10)
+    assert stat <= STAT_TOL and upd <= UPD_TOL
+
+
+@pytest.mark.parametrize("shapes", [[(96, 160)], [(160, 96)], [(128, 128)]], ids=str)
+def test_zero_statistics(shapes):
+    upd, stat = _run(shapes, seed=41, stats="zero", iters=12, beta2=1.0)
+    assert stat <= STAT_TOL and upd <= UPD_TOL
+
+
+def test_three_steps():
+    upd, stat = _run([(200, 300), (300, 200)], seed=51, iters=8, steps=3)
+    assert stat <= STAT_TOL and upd <= UPD_TOL
+
+
+def test_large_matrix():
+    """Several 256-tiles on each side and a ragged edge: 1000 x 2000, 20 root iterations."""
+    upd, stat = _run([(1000, 2000)], seed=61, iters=20)
+    assert stat <= STAT_TOL and upd <= UPD_TOL
+
+
+def test_empty_list_is_a_noop():
+    nm.ShampooStep([], [], [], [])()
+    torch.cuda.synchronize()
+
+
+def test_workspace_too_small():
+    shapes = [(64, 96)]
+    items = list(W.shampoo_inputs(shapes, 1))
+    ts = [[t.to(DEV) for t in x] for x in items]
+    ws = torch.empty(1024, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError):
+        nm.ShampooStep([t[0] for t in ts], [t[1] for t in ts], [t[2] for t in ts], [t[3] for t in ts],
+                       workspace=ws)
+    step = nm.ShampooStep([t[0] for t in ts], [t[1] for t in ts], [t[2] for t in ts], [t[3] for t in ts])
+    with pytest.raises(nm.MuonError) as ei:
+        nm.shampoo_step_raw(step.arr, 1, step.hp, step.workspace.data_ptr(), step.ws_bytes - 256,
+                            nm._stream_handle(None, step.device))
+    assert ei.value.status == nm.MUON_ENOSPC
