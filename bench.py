@@ -12,7 +12,12 @@ Prints one JSON line:
   cpu_baseline   the float64 CPU oracle on a bounded sample of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       python bench.py --optimizer shampoo [--workload shampoo_layer4096_f32]
        python bench.py --copy-calibration BYTES   (plain copy kernel, for HBM counters)
+
+With --optimizer shampoo one step is one shampoo_step over the workload's fp32 matrices
+(statistics, both inverse fourth roots by coupled Newton steps, the update); value is its
+algorithmic TFLOP/s and the roofline compares the fp32 MFMA kernel with the fp32 peak.
 """
 
 from __future__ import annotations
@@ -117,6 +122,140 @@ def cpu_baseline(wl, budget_s: float = 30.0):
     }
 
 
+def cpu_baseline_shampoo(wl, budget_s: float = 30.0):
+    """Time the CPU oracle's inverse fourth root on a bounded sample: the left statistic of the
+    workload's first matrix, with as many coupled Newton steps as fit in about ``budget_s``
+    seconds (one step timed first).  Flops follow the rule of value: 4 m(m+1)m per step."""
+    import numpy as np
+
+    from oracle.shampoo_oracle import inverse_root_newton, root_scale
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((d.get("num_threads", 1) for d in threadpool_info()
+                       if d.get("user_api") == "blas"), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    _, _, L0, _ = next(iter(wl.generate()))
+    A = L0.double().numpy() + wl.eps * np.eye(L0.shape[0])
+    nu = root_scale(L0.double().numpy(), wl.eps)
+    m = A.shape[0]
+    t0 = time.perf_counter()
+    inverse_root_newton(A, nu, 1)
+    one = time.perf_counter() - t0
+    iters = max(1, min(wl.root_iters, int((budget_s - one) / max(one, 1e-9))))
+    t0 = time.perf_counter()
+    inverse_root_newton(A, nu, iters)
+    spent = time.perf_counter() - t0
+    flops = 4.0 * iters * m * (m + 1) * m
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"float64 coupled-Newton inverse fourth root of one {m}x{m} statistic, {iters} of "
+                  f"{wl.root_iters} steps, {spent:.1f} s; flops counted with the same rule as value",
+        "seconds": spent,
+    }
+
+
+def bench_shampoo(args) -> int:
+    import torch
+
+    import newton_schulz_02_amd as nm
+    from newton_schulz_02_amd import workloads as W
+
+    name = args.workload if args.workload in W.SHAMPOO_WORKLOADS else "shampoo_layer4096_f32"
+    wl = W.SHAMPOO_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    print(f"[bench] workload {wl.name}: {wl.count} matrices; drawing inputs", file=sys.stderr, flush=True)
+    params, grads, lefts, rights = [], [], [], []
+    for w, g, lt, rt in wl.generate(device=dev):
+        params.append(w)
+        grads.append(g)
+        lefts.append(lt)
+        rights.append(rt)
+    step = nm.ShampooStep(params, grads, lefts, rights, lr=wl.lr, beta2=wl.beta2, eps=wl.eps,
+                          root_iters=wl.root_iters)
+    plan = step.plan()
+    flops = plan["flops"]
+    stream = torch.cuda.current_stream(dev)
+    print(f"[bench] {len(plan['launches'])} launches per step, workspace {step.ws_bytes / 2**30:.2f} GiB",
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(stream)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+    nm.profile_begin()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    stats = nm.profile_end()
+    ms = start.elapsed_time(stop) / args.steps
+    value = flops / (ms * 1e-3) / 1e12
+    gs = stats["gemm_f32"]
+    avg_ms = gs["ms"] / gs["launches"]
+    flops_per_launch = gs["flops"] / gs["launches"]
+    achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
+    kernels = {k: {"launches": v["launches"] // args.steps, "ms_per_step": v["ms"] / args.steps,
+                   "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None,
+                   "gbs": (v["bytes"] / (v["ms"] * 1e-3) / 1e9) if v["bytes"] else None}
+               for k, v in stats.items()}
+    print(f"[bench] {ms:.3f} ms/step; per kernel: {json.dumps(kernels)}", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_shampoo(wl, args.cpu_budget)
+    out = {
+        "metric": "Shampoo step TFLOP/s, % of fp32 MFMA peak (1 GPU)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "matrices_per_s": round(wl.count / (ms * 1e-3), 3),
+        "pct_of_f32_peak": round(100.0 * value / F32_PEAK_TFLOPS, 2),
+        "algorithmic_flops_per_step": flops,
+        "config": {
+            "workload": wl.name,
+            "matrices": wl.count,
+            "shapes": sorted({f"{r}x{c}" for r, c in wl.shapes}),
+            "root_iters": wl.root_iters,
+            "beta2": wl.beta2,
+            "eps": wl.eps,
+            "launches_per_step": len(plan["launches"]),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_f32",
+            "achieved": round(achieved, 2),
+            "peak": F32_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / F32_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "launches_per_step": gs["launches"] // args.steps,
+            "avg_launch_ms": round(avg_ms, 5),
+            "flops_per_launch": flops_per_launch,
+        },
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def algorithmic_flops_one(m: int, n: int, wl) -> float:
     import newton_schulz_02_amd as nm
 
@@ -143,6 +282,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--optimizer", choices=["muon", "shampoo"], default="muon")
     ap.add_argument("--workload", default="layer4096_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
@@ -163,6 +303,8 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return 0
+    if args.optimizer == "shampoo":
+        return bench_shampoo(args)
 
     import torch
 

@@ -212,14 +212,25 @@ def generate_tail(wl: Workload, device=None):
 
 # --- Shampoo inputs ----------------------------------------------------------------------
 
-def _spd(rng: np.random.Generator, n: int, scale: float, cond: float) -> np.ndarray:
-    """Q diag(lam) Q^T: Q Haar-orthogonal (QR of a Gaussian, column signs fixed by R's
-    diagonal), lam log-uniform over [scale / cond, scale], in float64."""
-    Q, R = np.linalg.qr(rng.standard_normal((n, n)))
-    Q = Q * np.sign(np.where(np.diag(R) == 0, 1.0, np.diag(R)))
+def _spd(rng: np.random.Generator, n: int, scale: float, cond: float, reflections: int = 8) -> np.ndarray:
+    """Q diag(lam) Q^T in float64 with lam log-uniform over [scale / cond, scale] and Q the
+    product of `reflections` Householder reflections I - 2 v v^T (v Gaussian, normalised).
+
+    H S H = S - v w^T - w v^T with u = S v, w = 2 u - 2 (v^T u) v: one symmetric matrix-vector
+    product and one symmetric rank-2 update per reflection, on the upper triangle (BLAS
+    dsymv and dsyr2), so large statistics cost O(n^2)."""
+    from scipy.linalg import blas
+
     lam = scale * np.exp(rng.uniform(-np.log(cond), 0.0, n))
-    S = (Q * lam) @ Q.T
-    return (S + S.T) / 2
+    S = np.asfortranarray(np.diag(lam))
+    for _ in range(reflections):
+        v = rng.standard_normal(n)
+        v /= np.linalg.norm(v)
+        u = blas.dsymv(1.0, S, v, lower=0)
+        w = 2.0 * u - 2.0 * float(v @ u) * v
+        S = blas.dsyr2(-1.0, v, w, a=S, lower=0, overwrite_a=1)
+    U = np.triu(S)
+    return U + np.triu(U, 1).T
 
 
 def shampoo_inputs(shapes, seed: int, *, grad_std: float = 1e-2, weight_std: float = 0.02,
@@ -230,7 +241,8 @@ def shampoo_inputs(shapes, seed: int, *, grad_std: float = 1e-2, weight_std: flo
     as float32 normals times weight_std and grad_std, then (``stats="warm"``) the left and
     the right statistic as symmetric positive definite matrices Q diag(lam) Q^T with lam
     log-uniform over [s / cond, s], s = grad_std^2 max(rows, cols) (the size of the
-    eigenvalues of one G G^T), rounded to float32 and made exactly symmetric; or zero
+    eigenvalues of one G G^T) and Q a product of 8 Householder reflections, rounded to
+    float32 and made exactly symmetric; or zero
     statistics (``stats="zero"``, a first step).
     """
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -249,3 +261,47 @@ def shampoo_inputs(shapes, seed: int, *, grad_std: float = 1e-2, weight_std: flo
         else:
             raise ValueError(f"stats must be 'warm' or 'zero', not {stats!r}")
         yield W, G, L0, R0
+
+
+@dataclass(frozen=True)
+class ShampooWorkload:
+    """Inputs of a Shampoo step: shapes, seed and distributions (see shampoo_inputs) and the
+    hyperparameters it runs with."""
+    name: str
+    description: str
+    seed: int
+    shapes: tuple
+    grad_std: float = 1e-3
+    weight_std: float = 0.02
+    stats: str = "warm"
+    cond: float = 1e3
+    lr: float = 1e-3
+    beta2: float = 0.9
+    eps: float = 1e-6
+    root_iters: int = 12
+
+    @property
+    def count(self) -> int:
+        return len(self.shapes)
+
+    def generate(self, device=None):
+        for W, G, L0, R0 in shampoo_inputs(self.shapes, self.seed, grad_std=self.grad_std,
+                                           weight_std=self.weight_std, stats=self.stats, cond=self.cond):
+            if device is not None:
+                W, G, L0, R0 = W.to(device), G.to(device), L0.to(device), R0.to(device)
+            yield W, G, L0, R0
+
+
+SHAMPOO_WORKLOADS = {
+    "shampoo_layer4096_f32": ShampooWorkload(
+        name="shampoo_layer4096_f32",
+        description="one 4096-hidden decoder layer (Q,K,V,O 4096x4096, gate/up 4096x11008, down "
+                    "11008x4096) in fp32, G ~ N(0, 1e-3^2), warm statistics (condition 1e3), "
+                    "12 coupled Newton steps per root",
+        seed=7, shapes=tuple((s.rows, s.cols) for s in layer_shapes())),
+    "shampoo_attn4096_f32": ShampooWorkload(
+        name="shampoo_attn4096_f32",
+        description="the four 4096x4096 attention matrices of one 4096-hidden layer in fp32, "
+                    "G ~ N(0, 1e-3^2), warm statistics (condition 1e3), 12 coupled Newton steps per root",
+        seed=8, shapes=((4096, 4096),) * 4),
+}

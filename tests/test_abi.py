@@ -16,7 +16,7 @@ import pytest
 
 import newton_schulz_02_amd as nm
 
-HEADER = Path(__file__).resolve().parents[1] / "include" / "muon.h"
+HEADERS = sorted((Path(__file__).resolve().parents[1] / "include").glob("*.h"))
 
 
 def _gpu_visible() -> bool:
@@ -29,16 +29,18 @@ def _gpu_visible() -> bool:
 
 
 def declared_functions():
-    text = HEADER.read_text()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_]+)\s*\(", text, flags=re.M)
-    return sorted(set(n for n in names if n.startswith(("muon_", "adamw_"))))
+    names = []
+    for header in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", header.read_text(), flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_]+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n.startswith(("muon_", "adamw_", "shampoo_"))))
 
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"muon_step", "muon_workspace_size", "adamw_step", "muon_strerror",
-            "muon_last_error", "muon_profile_begin", "muon_profile_end"} <= set(names)
+            "muon_last_error", "muon_profile_begin", "muon_profile_end", "shampoo_step",
+            "shampoo_workspace_size", "shampoo_plan_describe"} <= set(names)
     lib = nm.lib()
     for name in names:
         assert hasattr(lib, name), name
