@@ -103,6 +103,7 @@ _SIGNATURES = {
     "muon_tune_import": (c_int, [c_char_p]),
     "muon_debug_wide_tile_order": (c_int, [c_int, c_int, c_int, POINTER(c_int), POINTER(c_int)]),
     "muon_debug_split": (c_int, [c_int, c_int, c_int, POINTER(c_int), POINTER(c_int), c_int]),
+    "muon_debug_flat_loads": (c_int, [c_int32]),
     "shampoo_workspace_size": (c_int, [_SMATP, c_int32, _SHPP, POINTER(c_size_t)]),
     "shampoo_step": (c_int, [_SMATP, c_int32, _SHPP, c_void_p, c_size_t, c_void_p]),
     "shampoo_plan_describe": (c_int, [_SMATP, c_int32, _SHPP, c_char_p, c_size_t]),
@@ -372,6 +373,12 @@ def split_plan(tiles: int, units: int, ksteps: int):
     keys = ("mode", "pieces_or_n", "dp_tiles", "tail", "tail_wgs", "slots")
     out = [None if items[5 * j] < 0 else tuple(items[5 * j:5 * j + 5]) for j in range(n)]
     return dict(zip(keys, plan[:6])), out
+
+
+def flat_loads(on: bool) -> None:
+    """Test hook: 64-bit operand pointers in every 256 x 256 launch (the path of operands of
+    2 GB and more) instead of 32-bit buffer offsets."""
+    _check(lib().muon_debug_flat_loads(1 if on else 0))
 
 
 def xcd_remap(total: int):

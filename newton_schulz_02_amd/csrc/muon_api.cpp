@@ -66,6 +66,9 @@ std::vector<Rec> g_recs;
 // a forced configuration for every launch (-1: none).
 std::map<std::string, int> g_tune;
 int g_force_cfg = -1;
+// Test hook: run every 256 x 256 launch with 64-bit operand pointers (the path of operands of
+// 2 GB and more).
+bool g_flat_loads = false;
 
 // Caller holds g_mu.
 int choose_cfg(const std::string& sig) {
@@ -217,6 +220,7 @@ int run_launch(int dev, hipStream_t s, const Plan& plan, const PlanLaunch& L, in
   a.split_cnt = split_cnt;
   a.split_slots = reinterpret_cast<float*>(ws + plan.split_slot_off);
   a.grid = a.dp_tiles + a.tail_wgs;
+  a.buf32 = (L.buf_ok && !g_flat_loads) ? 1 : 0;
   if (split && (sp.tail > plan.split_cnt_n / 2 || sp.slots > plan.split_slots))
     return fail(MUON_EINVAL, "internal: tail split exceeds its workspace");
   const bool bf = L.dtype == kBF16;
@@ -578,6 +582,12 @@ int muon_debug_split(int tiles, int units, int ksteps, int* plan, int* items, in
     std::memcpy(items + 5 * j, it, sizeof it);
   }
   return sp.tail_wgs;
+}
+
+int muon_debug_flat_loads(int32_t on) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_flat_loads = on != 0;
+  return MUON_OK;
 }
 
 int muon_tune_force(int32_t cfg) {

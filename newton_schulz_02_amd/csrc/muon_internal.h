@@ -112,6 +112,8 @@ struct GemmArgs {
   int32_t ngroups;
   int32_t total_tiles;   // output tiles of the launch
   int32_t grid;          // workgroups of the launch (total_tiles unless the tail is split)
+  int32_t buf32;         // launcher only: every operand is below 2 GB, so the 256 x 256 kernel
+                         // may address operands with 32-bit buffer offsets
   GroupArg g[kMaxGroups];
   // Tail split (tile_order.h): the first dp_tiles workgroups run whole tiles (all of them
   // when split_mode is kSplitNone), the next tail_wgs run pieces of the last tail_tiles.

@@ -335,6 +335,7 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
     {  // largest operand, with a tile's overhang of rows, below 2^31 bytes
       const int64_t big = std::max(p.m, p.n);
       p.wide_ok = (big + kWideN) * round_up(big, kKPad) * int64_t(p.gsize) < (int64_t(1) << 31);
+      p.buf_ok = big * round_up(big, kKPad) * int64_t(p.gsize) < (int64_t(1) << 31);
     }
     // Momentum tiles cover the extents rounded up to kKPad, so that the zero padding of the
     // row and transposed copies (leading dimensions rounded to kKPad) is written too.
@@ -486,7 +487,10 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
           a.alpha = g.op.alpha;
           a.tri = g.op.tri;
           a.nm = (g.op.kind == kOpUpdate && p0.tall) ? 1 : 0;  // W is n x m
-          for (int i = g.first; i < g.last; ++i) L.wide_ok = L.wide_ok && plan->mats[i].wide_ok;
+          for (int i = g.first; i < g.last; ++i) {
+            L.wide_ok = L.wide_ok && plan->mats[i].wide_ok;
+            L.buf_ok = L.buf_ok && plan->mats[i].buf_ok;
+          }
           for (int sh = 0; sh < kNumShapes; ++sh) {
             a.tile_begin = int32_t(L.tiles_cfg[sh]);
             for (int i = g.first; i < g.last; ++i) {
@@ -695,6 +699,7 @@ std::string describe_plan(const Plan& plan) {
     }
     os << "]"
        << ",\"wide_ok\":" << (L.wide_ok ? "true" : "false")
+       << ",\"buf_ok\":" << (L.buf_ok ? "true" : "false")
        << ",\"signature\":\"" << L.signature << "\",\"flops\":" << L.flops
        << ",\"groups\":[";
     for (size_t g = 0; g < L.groups.size(); ++g) {

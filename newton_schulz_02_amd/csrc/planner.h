@@ -41,6 +41,7 @@ struct PlanMat {
   // their prefixes over the sorted order.
   int64_t wide_tiles[3] = {0, 0, 0}, wide_prefix[3] = {0, 0, 0};
   bool wide_ok = true;  // every operand fits the 256 x 384 kernel's 32-bit buffer offsets
+  bool buf_ok = true;   // every operand (rows x leading dimension) is below 2 GB
   double flops = 0, bytes = 0;
 };
 
@@ -68,6 +69,7 @@ struct PlanLaunch {
   int kmin_cfg[kNumShapes] = {0, 0};   // gemm: fewest k-steps among the last kMaxUnits tiles
   SplitPlan split_cfg[kNumShapes];     // gemm: tail split under each tile shape
   bool wide_ok = true;           // gemm: the 256 x 384 configuration may run this launch
+  bool buf_ok = true;            // gemm: every operand is below 2 GB (32-bit buffer offsets)
   bool own_coef = false;         // gemm: pa, pb, pc below (else the Newton-Schulz a, b, c)
   float pa = 0.0f, pb = 0.0f, pc = 0.0f;
   std::string signature;         // gemm: shapes and ops of the launch (the tuning key)

@@ -389,6 +389,12 @@ int build_shampoo_plan(const shampoo_matrix* mats, int32_t count, const shampoo_
     L.last = last;
     L.cfg = kCfgSquare;
     L.wide_ok = false;
+    // Operands: the statistic slots (m x round_up(m)) or the copies of G, G^T and X_L G.
+    for (int e = first; e < last; ++e) {
+      const PlanMat& p = plan.mats[size_t(e)];
+      const int64_t big = e >= count ? p.m * p.mp : std::max(p.r * p.np, p.c * p.mp);
+      L.buf_ok = L.buf_ok && big * 4 < (int64_t(1) << 31);
+    }
     L.own_coef = true;
     L.pa = cf.pa;
     L.pb = cf.pb;
@@ -626,7 +632,7 @@ std::string describe_shampoo_plan(const ShampooPlan& sp) {
     const PlanLaunch& L = plan.launches[i];
     os << (i ? "," : "") << "{\"kind\":\"" << kLaunch[L.kind] << "\",\"level\":" << L.level
        << ",\"first\":" << L.first << ",\"last\":" << L.last << ",\"tiles\":" << L.tiles
-       << ",\"grid\":" << L.grid << ",\"flops\":" << L.flops << ",\"coef\":[" << L.pa << "," << L.pb
+       << ",\"grid\":" << L.grid << ",\"buf_ok\":" << (L.buf_ok ? "true" : "false") << ",\"flops\":" << L.flops << ",\"coef\":[" << L.pa << "," << L.pb
        << "," << L.pc << "],\"groups\":[";
     for (size_t g = 0; g < L.groups.size(); ++g) {
       const GroupArg& a = L.groups[g];

@@ -236,3 +236,13 @@ def test_aliasing():
     arr = nm.shampoo_shape_array([(8, 8), (8, 8)])
     arr[1].grad = arr[0].grad  # two matrices may read one gradient
     assert _status(arr, 2, hp) == nm.MUON_OK
+
+
+def test_buffer_offsets_flag():
+    """Launches address operands with 32-bit buffer offsets only while every operand is below 2 GB."""
+    hp = nm.make_shampoo_hparams(root_iters=2)
+    small = nm.shampoo_plan_describe(nm.shampoo_shape_array([(300, 200)]), 1, hp)
+    assert all(L["buf_ok"] for L in small["launches"] if L["kind"] == "gemm")
+    big = nm.shampoo_plan_describe(nm.shampoo_shape_array([(8, 23200)]), 1, hp)  # 23200^2 fp32 > 2 GB
+    flags = {(L["first"], L["last"]): L["buf_ok"] for L in big["launches"] if L["kind"] == "gemm"}
+    assert flags[(1, 3)] is False and flags[(0, 1)] is True

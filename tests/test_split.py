@@ -252,3 +252,15 @@ def test_workspace_holds_the_partial_sums():
     # Small calls reserve little: one 64 x 64 matrix has no tail to cut.
     d, _ = _gemms([(64, 64)])
     assert d["split_slots"] == 0
+
+
+def test_buffer_offsets_flag():
+    """The 256 x 256 kernel uses 32-bit buffer offsets only while every operand of a launch is
+    below 2 GB: a 32768 x 32768 bf16 matrix (2 GiB operands) turns it off for its launches."""
+    hp = nm.make_hparams()
+    small = nm.plan_describe(nm.shape_array([(4096, 11008)]), 1, hp)
+    assert all(L["buf_ok"] for L in small["launches"] if L["kind"] == "gemm")
+    big = nm.plan_describe(nm.shape_array([(32768, 32768)]), 1, hp)
+    assert not any(L["buf_ok"] for L in big["launches"] if L["kind"] == "gemm")
+    mixed = nm.plan_describe(nm.shape_array([(32768, 32768), (512, 512)]), 2, hp)
+    assert not any(L["buf_ok"] for L in mixed["launches"] if L["kind"] == "gemm")
