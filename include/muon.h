@@ -156,7 +156,11 @@ int muon_owner_assign(const double* cost, int32_t count, int32_t ranks, int64_t 
  * for a signature the table does not hold.  The table is shared by all threads and devices.
  * Configuration 1 addresses operands with 32-bit offsets: a launch holding a matrix whose
  * larger side d has (d + 384) * (d rounded up to 128) * element size >= 2^31 bytes always
- * runs configuration 0 (or 2), whatever the table or muon_tune_force say.
+ * runs configuration 0 (or 2), whatever the table or muon_tune_force say.  An fp32 launch
+ * (fp32 matrices, and bf16 ones with at most 128 Gram rows) whose last tiles contract over
+ * 2^17 elements or more always runs with the tail split (2 or 3), whatever the table or
+ * muon_tune_force say: each piece sums at most an eighth of the contraction, which keeps the
+ * fp32 rounding of 2^20-long contractions within the 1e-4 bar.
  *
  * muon_tune: runs one step over device copies of the list's params and momenta (the
  *   caller's matrices are not modified).  After each MFMA launch of that step it times the

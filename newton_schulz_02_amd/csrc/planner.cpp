@@ -564,6 +564,8 @@ void plan_splits(Plan* plan, int units) {
     int cfg = L.cfg;
     if (cfg < 0 || cfg >= kNumCfg) cfg = kCfgSquare;
     if (cfg_shape(cfg) == kCfgWide && !L.wide_ok) cfg &= ~1;
+    // Long fp32 contractions always run split (accuracy: see kF32SplitMinK).
+    if (L.dtype == kF32 && int64_t(L.kmin_cfg[cfg_shape(cfg)]) * 32 >= kF32SplitMinK) cfg |= 2;
     if (cfg_split(cfg) && L.split_cfg[cfg_shape(cfg)].mode == kSplitNone) cfg &= ~2;
     L.cfg = cfg;
     const int sh = cfg_shape(cfg);

@@ -117,6 +117,15 @@ void fill_descs(const Plan& plan, const muon_matrix* mats, const muon_hparams* h
 // Gram formation and update then run in the fp32 kernel on fp32 copies of X, and the update
 // rounds W back to bf16.
 constexpr int64_t kF32GramMaxM = 128;
+
+// fp32 launches whose tail tiles contract over at least this many elements run with the tail
+// split whatever the chosen configuration: the MFMA accumulates a tile's products in fp32 in
+// sequence, so its rounding error grows as the square root of the contraction length; at
+// 2^20 (the longest side allowed) that took a 3 x 2^20 fp32 matrix to 1.3e-4 relative error
+// against the 1e-4 bar.  Split pieces keep separate fp32 sums of at most an eighth of the
+// contraction each, added in piece order, and the launch (a Gram formation of at most 136
+// tiles for m <= 4096: all of them tail tiles) spreads over more compute units.
+constexpr int64_t kF32SplitMinK = int64_t(1) << 17;
 int gram_dtype(int dtype, int64_t m);
 
 // Resolve the restart set of one matrix (bit k = re-anchor before iteration k).

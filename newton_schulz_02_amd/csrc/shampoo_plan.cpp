@@ -389,10 +389,12 @@ int build_shampoo_plan(const shampoo_matrix* mats, int32_t count, const shampoo_
     L.last = last;
     L.cfg = kCfgSquare;
     L.wide_ok = false;
-    // Operands: the statistic slots (m x round_up(m)) or the copies of G, G^T and X_L G.
+    // Operands: the statistic slots (m x round_up(m)); for a matrix, the copies of G, G^T and
+    // X_L G and the roots X_L and X_R it reads from its statistics' slots.
     for (int e = first; e < last; ++e) {
       const PlanMat& p = plan.mats[size_t(e)];
-      const int64_t big = e >= count ? p.m * p.mp : std::max(p.r * p.np, p.c * p.mp);
+      const int64_t big = e >= count ? p.m * p.mp
+                                     : std::max({p.r * p.np, p.c * p.mp, p.r * p.mp, p.c * p.np});
       L.buf_ok = L.buf_ok && big * 4 < (int64_t(1) << 31);
     }
     L.own_coef = true;

@@ -243,6 +243,12 @@ def test_buffer_offsets_flag():
     hp = nm.make_shampoo_hparams(root_iters=2)
     small = nm.shampoo_plan_describe(nm.shampoo_shape_array([(300, 200)]), 1, hp)
     assert all(L["buf_ok"] for L in small["launches"] if L["kind"] == "gemm")
-    big = nm.shampoo_plan_describe(nm.shampoo_shape_array([(8, 23200)]), 1, hp)  # 23200^2 fp32 > 2 GB
-    flags = {(L["first"], L["last"]): L["buf_ok"] for L in big["launches"] if L["kind"] == "gemm"}
-    assert flags[(1, 3)] is False and flags[(0, 1)] is True
+    # A 23200 x 23200 fp32 statistic is over 2 GB: its launches, and the matrix's own launches
+    # (X_L G and the update read the roots in the statistics' slots), use 64-bit pointers.
+    big = nm.shampoo_plan_describe(nm.shampoo_shape_array([(8, 23200)]), 1, hp)
+    assert not any(L["buf_ok"] for L in big["launches"] if L["kind"] == "gemm")
+    tall = nm.shampoo_plan_describe(nm.shampoo_shape_array([(23200, 8)]), 1, hp)
+    assert not any(L["buf_ok"] for L in tall["launches"] if L["kind"] == "gemm")
+    # 23168^2 x 4 bytes < 2^31: every launch keeps the buffer path
+    edge = nm.shampoo_plan_describe(nm.shampoo_shape_array([(8, 23168)]), 1, hp)
+    assert all(L["buf_ok"] for L in edge["launches"] if L["kind"] == "gemm")

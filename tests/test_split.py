@@ -264,3 +264,28 @@ def test_buffer_offsets_flag():
     assert not any(L["buf_ok"] for L in big["launches"] if L["kind"] == "gemm")
     mixed = nm.plan_describe(nm.shape_array([(32768, 32768), (512, 512)]), 2, hp)
     assert not any(L["buf_ok"] for L in mixed["launches"] if L["kind"] == "gemm")
+
+
+def test_long_fp32_contractions_always_split():
+    """fp32 Gram formations over 2^17 or more elements run split whatever the configuration
+    asked for (accuracy of the fp32 sums); shorter ones and bf16 ones follow the request."""
+    hp = nm.make_hparams()
+    try:
+        nm.tune_force(nm.CFG_SQUARE)
+        long = nm.plan_describe(nm.shape_array([(3, 1 << 20, nm.MUON_F32)]), 1, hp)
+        syrk = long["launches"][2]
+        assert syrk["groups"][0]["kind"] == "syrk" and syrk["cfg"] == nm.CFG_SQUARE_SPLIT
+        assert syrk["split_cfg"][0]["mode"] == 1 and syrk["split_cfg"][0]["c"] == 8
+        assert all(L["cfg"] == nm.CFG_SQUARE for L in long["launches"][3:] if L["kind"] == "gemm")
+        thin_bf16 = nm.plan_describe(nm.shape_array([(3, 1 << 20, nm.MUON_BF16)]), 1, hp)
+        assert thin_bf16["launches"][2]["cfg"] == nm.CFG_SQUARE_SPLIT  # fp32 Gram space (m <= 128)
+        short = nm.plan_describe(nm.shape_array([(3, 1 << 16, nm.MUON_F32)]), 1, hp)
+        assert all(L["cfg"] == nm.CFG_SQUARE for L in short["launches"] if L["kind"] == "gemm")
+        bf16 = nm.plan_describe(nm.shape_array([(256, 1 << 20, nm.MUON_BF16)]), 1, hp)
+        assert all(L["cfg"] == nm.CFG_SQUARE for L in bf16["launches"] if L["kind"] == "gemm")
+        # 256 x 384 tiles are out at this length (32-bit offsets): the split runs on 256 x 256
+        nm.tune_force(nm.CFG_WIDE)
+        wide = nm.plan_describe(nm.shape_array([(3, 1 << 20, nm.MUON_F32)]), 1, hp)
+        assert wide["launches"][2]["cfg"] == nm.CFG_SQUARE_SPLIT
+    finally:
+        nm.tune_force(None)
