@@ -176,6 +176,10 @@ def bench_shampoo(args) -> int:
         grads.append(g)
         lefts.append(lt)
         rights.append(rt)
+    # The statistics' launches run the tail split where they have a partial last round
+    # (default); --kernel square turns it off, for comparison.
+    nm.tune_force({"tuned": None, "square": nm.CFG_SQUARE, "wide": nm.CFG_SQUARE,
+                   "square-split": nm.CFG_SQUARE_SPLIT, "wide-split": nm.CFG_SQUARE_SPLIT}[args.kernel])
     step = nm.ShampooStep(params, grads, lefts, rights, lr=wl.lr, beta2=wl.beta2, eps=wl.eps,
                           root_iters=wl.root_iters)
     plan = step.plan()
@@ -236,6 +240,8 @@ def bench_shampoo(args) -> int:
             "beta2": wl.beta2,
             "eps": wl.eps,
             "launches_per_step": len(plan["launches"]),
+            "split_launches": sum(1 for L in plan["launches"] if L["kind"] == "gemm" and L["cfg"] & 2),
+            "kernel_selection": "256x256, tail split" if args.kernel == "tuned" else args.kernel,
         },
         "roofline": {
             "bound": "mfma",

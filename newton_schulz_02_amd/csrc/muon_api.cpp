@@ -483,8 +483,10 @@ int shampoo_plan_describe(const shampoo_matrix* mats, int32_t count, const shamp
     if (!buf || len == 0) return fail(MUON_EINVAL, "buf is NULL or empty");
     ShampooPlan sp;
     std::string err;
+    std::lock_guard<std::mutex> lock(g_mu);
     const int rc = build_shampoo_plan(mats, count, hp, &sp, &err);
     if (rc != MUON_OK) return fail(rc, err);
+    shampoo_plan_splits(&sp, kMaxUnits, g_force_cfg);
     const std::string s = describe_shampoo_plan(sp);
     const size_t n = std::min(len - 1, s.size());
     std::memcpy(buf, s.data(), n);
@@ -520,6 +522,7 @@ int shampoo_step(const shampoo_matrix* mats, int32_t count, const shampoo_hparam
     int dev = 0;
     if ((rc = current_device(&dev)) != MUON_OK) return rc;
     if ((rc = check_device(dev)) != MUON_OK) return rc;
+    shampoo_plan_splits(&sp, g_dev[dev].units, g_force_cfg);
     rc = upload(dev, descs.data(), descs.size() * sizeof(MatDesc), ws + sp.plan.desc_off, s);
     if (rc != MUON_OK) return rc;
     // The launches read only eps (the norm) and beta (unused: no momentum buffer) from here.

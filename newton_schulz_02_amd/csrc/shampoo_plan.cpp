@@ -354,8 +354,9 @@ int build_shampoo_plan(const shampoo_matrix* mats, int32_t count, const shampoo_
   off = align_up(off + entries * 4);
   plan.partial_off = off;
   off = align_up(off + mom * 4);
-  plan.split_cnt_off = off;  // no tail split: no counters
-  plan.split_cnt_n = 0;
+  plan.split_cnt_off = off;  // tail split: 2 counters per tail tile
+  plan.split_cnt_n = 2 * kMaxUnits;
+  off = align_up(off + int64_t(plan.split_cnt_n) * 4);
   for (int i = 0; i < count; ++i) {
     PlanMat& p = plan.mats[size_t(i)];
     for (int64_t& o : p.off) o = -1;
@@ -374,7 +375,7 @@ int build_shampoo_plan(const shampoo_matrix* mats, int32_t count, const shampoo_
       off = align_up(off + p.m * p.mp * 4);
     }
   }
-  plan.split_slot_off = off;
+  plan.split_slot_off = off;  // the partial-sum slots go last, sized once the launches are known
   plan.split_slots = 0;
   plan.ws_bytes = size_t(off);
   if (count == 0) return MUON_OK;
@@ -413,11 +414,33 @@ int build_shampoo_plan(const shampoo_matrix* mats, int32_t count, const shampoo_
     }
     L.groups_cfg[0].push_back(a);
   };
+  // K-steps of one tile of group a on entry e: the contraction (padded) over 32 fp32 values.
+  auto ksteps = [&](const GroupArg& a, int e) -> int {
+    const PlanMat& p = plan.mats[size_t(e)];
+    if (a.kind == kOpAffine) return 0;
+    if (e < count) return int((a.kind == kOpXform ? p.mp : p.np) / 32);  // X_L G over rows, Z X_R over cols
+    if (a.kind == kOpPoly) {  // F F^T over the other side of the matrix
+      const PlanMat& g = plan.mats[size_t(p.orig)];
+      return int((sp->stat_right[size_t(e - count)] ? g.mp : g.np) / 32);
+    }
+    return int(p.mp / 32);
+  };
   auto finish = [&](PlanLaunch& L, const char* what) {
     L.groups = L.groups_cfg[0];
     L.tiles = L.tiles_cfg[0];
     L.grid = L.tiles;
     L.signature = what;
+    // Fewest k-steps among the tiles a tail split may cut (the last kMaxUnits).
+    const int64_t from = std::max<int64_t>(0, L.tiles - kMaxUnits);
+    int64_t end = 0;
+    int kmin = INT_MAX;
+    for (const GroupArg& a : L.groups_cfg[0])
+      for (int e = a.first; e < a.last; ++e) {
+        const PlanMat& p = plan.mats[size_t(e)];
+        end += a.tri ? p.tri_tiles : p.full_tiles;
+        if (end > from) kmin = std::min(kmin, ksteps(a, e));
+      }
+    L.kmin_cfg[0] = kmin == INT_MAX ? 0 : kmin;
     plan.launches.push_back(L);
   };
   auto code = [&](int v) -> int8_t {
@@ -529,13 +552,40 @@ int build_shampoo_plan(const shampoo_matrix* mats, int32_t count, const shampoo_
     }
     finish(L, "shampoo");
   }
+  // Partial-sum slots of the tail split, enough for any unit count up to kMaxUnits (as in the
+  // Muon plan).  The accumulation (level 0) runs before the norm kernel clears the split
+  // counters, so it is never split.
+  int64_t slots = 0;
   for (const PlanLaunch& L : plan.launches) {
-    if (L.kind == kLaunchGemm && L.tiles_cfg[0] > INT32_MAX) {
+    if (L.kind != kLaunchGemm) continue;
+    if (L.tiles_cfg[0] > INT32_MAX) {
       *err = "too many tiles in one launch";
       return MUON_EINVAL;
     }
+    if (L.level == 0 || L.kmin_cfg[0] / kSplitUnit < 4) continue;
+    const int64_t T = L.tiles_cfg[0];
+    slots = std::max(slots, std::max(std::min<int64_t>(2 * T, 2 * kMaxUnits),
+                                     std::min<int64_t>(kMaxPieces * T, kMaxUnits)));
   }
+  plan.split_slots = slots;
+  plan.ws_bytes = size_t(align_up(int64_t(plan.ws_bytes) + slots * kSlotFloats * 4));
+  shampoo_plan_splits(sp, kMaxUnits, -1);
   return MUON_OK;
+}
+
+void shampoo_plan_splits(ShampooPlan* sp, int units, int force_cfg) {
+  Plan& plan = sp->plan;
+  units = std::max(1, std::min(units, kMaxUnits));
+  plan.units = units;
+  for (PlanLaunch& L : plan.launches) {
+    if (L.kind != kLaunchGemm) continue;
+    L.split_cfg[0] = L.level == 0 ? SplitPlan() : plan_split(int(L.tiles_cfg[0]), units, L.kmin_cfg[0], kSplitUnit);
+    if (L.level == 0) L.split_cfg[0].dp_tiles = int(L.tiles_cfg[0]);
+    const bool want = force_cfg < 0 || cfg_split(force_cfg);
+    const SplitPlan& s = L.split_cfg[0];
+    L.cfg = (want && s.mode != kSplitNone) ? int(kCfgSquareSplit) : int(kCfgSquare);
+    L.grid = cfg_split(L.cfg) ? int64_t(s.dp_tiles) + s.tail_wgs : L.tiles;
+  }
 }
 
 void fill_shampoo_descs(const ShampooPlan& sp, const shampoo_matrix* mats,
@@ -612,6 +662,9 @@ std::string describe_shampoo_plan(const ShampooPlan& sp) {
      << ",\"slots\":" << sp.slots << ",\"stat_slot\":" << sp.stat_slot << ",\"root_slot\":" << sp.root_slot
      << ",\"desc_off\":" << plan.desc_off << ",\"scale_off\":" << plan.scale_off
      << ",\"partial_off\":" << plan.partial_off << ",\"mom_tiles\":" << plan.total_mom_tiles
+     << ",\"units\":" << plan.units << ",\"split_cnt_off\":" << plan.split_cnt_off
+     << ",\"split_cnt_n\":" << plan.split_cnt_n << ",\"split_slot_off\":" << plan.split_slot_off
+     << ",\"split_slots\":" << plan.split_slots
      << ",\"entries\":[";
   for (size_t e = 0; e < plan.mats.size(); ++e) {
     const PlanMat& p = plan.mats[e];
@@ -634,7 +687,12 @@ std::string describe_shampoo_plan(const ShampooPlan& sp) {
     const PlanLaunch& L = plan.launches[i];
     os << (i ? "," : "") << "{\"kind\":\"" << kLaunch[L.kind] << "\",\"level\":" << L.level
        << ",\"first\":" << L.first << ",\"last\":" << L.last << ",\"tiles\":" << L.tiles
-       << ",\"grid\":" << L.grid << ",\"buf_ok\":" << (L.buf_ok ? "true" : "false") << ",\"flops\":" << L.flops << ",\"coef\":[" << L.pa << "," << L.pb
+       << ",\"grid\":" << L.grid << ",\"cfg\":" << L.cfg << ",\"kmin\":" << L.kmin_cfg[0]
+       << ",\"split\":{\"mode\":" << L.split_cfg[0].mode << ",\"c\":" << L.split_cfg[0].c
+       << ",\"n\":" << L.split_cfg[0].n << ",\"dp_tiles\":" << L.split_cfg[0].dp_tiles
+       << ",\"tail\":" << L.split_cfg[0].tail << ",\"tail_wgs\":" << L.split_cfg[0].tail_wgs
+       << ",\"slots\":" << L.split_cfg[0].slots << "}"
+       << ",\"buf_ok\":" << (L.buf_ok ? "true" : "false") << ",\"flops\":" << L.flops << ",\"coef\":[" << L.pa << "," << L.pb
        << "," << L.pc << "],\"groups\":[";
     for (size_t g = 0; g < L.groups.size(); ++g) {
       const GroupArg& a = L.groups[g];

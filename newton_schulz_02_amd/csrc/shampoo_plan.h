@@ -49,6 +49,12 @@ struct ShampooPlan {
 int build_shampoo_plan(const shampoo_matrix* mats, int32_t count, const shampoo_hparams* hp,
                        ShampooPlan* sp, std::string* err);
 
+// Tail splits of the MFMA launches for `units` compute units (capped at kMaxUnits).
+// force_cfg < 0: split every launch that has a tail worth cutting (except the accumulation,
+// which runs before the split counters are cleared); otherwise split only when
+// cfg_split(force_cfg).  build_shampoo_plan calls it with kMaxUnits and -1.
+void shampoo_plan_splits(ShampooPlan* sp, int units, int force_cfg);
+
 // Fill the device descriptor table for a concrete workspace base address.
 void fill_shampoo_descs(const ShampooPlan& sp, const shampoo_matrix* mats,
                         const shampoo_hparams* hp, char* ws, std::vector<MatDesc>* out);

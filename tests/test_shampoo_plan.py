@@ -184,6 +184,8 @@ def test_workspace_regions_disjoint():
              (plan["partial_off"], plan["mom_tiles"] * 4)]
     for e in plan["entries"]:
         spans += [tuple(r) for r in e["regions"]]
+    spans += [(plan["split_cnt_off"], plan["split_cnt_n"] * 4),
+              (plan["split_slot_off"], plan["split_slots"] * 256 * 384 * 4)]
     spans.sort()
     for (a0, n0), (a1, _) in zip(spans, spans[1:]):
         assert a0 + n0 <= a1
@@ -252,3 +254,33 @@ def test_buffer_offsets_flag():
     # 23168^2 x 4 bytes < 2^31: every launch keeps the buffer path
     edge = nm.shampoo_plan_describe(nm.shampoo_shape_array([(8, 23168)]), 1, hp)
     assert all(L["buf_ok"] for L in edge["launches"] if L["kind"] == "gemm")
+
+
+def test_tail_split_of_the_statistics():
+    """Launches with a partial last round of long tiles run the tail split (the accumulation
+    excepted: it runs before the norm kernel clears the split counters); muon_tune_force 0
+    turns it off, 2 keeps it."""
+    shapes = [(4096, 4096)] * 4
+    hp = nm.make_shampoo_hparams(root_iters=3)
+    arr = nm.shampoo_shape_array(shapes)
+    plan = nm.shampoo_plan_describe(arr, 4, hp)
+    gemms = [L for L in plan["launches"] if L["kind"] == "gemm"]
+    assert gemms[0]["cfg"] == 0 and gemms[0]["split"]["mode"] == 0  # accumulation
+    prods = [L for L in gemms if any(g["kind"] in ("prod", "syrk") for g in L["groups"])]
+    assert prods and all(L["cfg"] == nm.CFG_SQUARE_SPLIT for L in prods)
+    for L in prods:  # 8 statistics x 136 tiles per group, 4096 / 32 k-steps
+        assert L["kmin"] == 128 and L["split"]["mode"] != 0
+        assert L["grid"] == L["split"]["dp_tiles"] + L["split"]["tail_wgs"]
+        assert L["split"]["slots"] <= plan["split_slots"] and L["split"]["tail"] <= plan["split_cnt_n"] // 2
+    affine = [L for L in gemms if L["groups"][0]["kind"] == "affine"]
+    assert all(L["cfg"] == 0 for L in affine)  # no contraction, nothing to cut
+    try:
+        nm.tune_force(nm.CFG_SQUARE)
+        off = nm.shampoo_plan_describe(arr, 4, hp)
+        assert all(L["cfg"] == 0 and L["grid"] == L["tiles"] for L in off["launches"] if L["kind"] == "gemm")
+        nm.tune_force(nm.CFG_SQUARE_SPLIT)
+        on = nm.shampoo_plan_describe(arr, 4, hp)
+        assert [L["cfg"] for L in on["launches"]] == [L["cfg"] for L in plan["launches"]]
+    finally:
+        nm.tune_force(None)
+    assert nm.shampoo_workspace_size_raw(arr, 4, hp) == plan["workspace"]
