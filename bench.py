@@ -304,7 +304,7 @@ def main() -> int:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the owner-side step needs no collective and "
-              "this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+              "this library has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
         return 2
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)

@@ -52,7 +52,7 @@ typedef enum muon_status {
   MUON_EALIAS = -3,      /* grad overlaps an output (param/momentum) of any matrix, or
                             outputs of two matrices overlap */
   MUON_EHIP = -4,        /* a HIP runtime call failed; muon_last_error() has the text */
-  MUON_EUNSUPPORTED = -5 /* valid request this build cannot run (e.g. no gfx950 device) */
+  MUON_EUNSUPPORTED = -5 /* valid request this library cannot run (e.g. no gfx950 device) */
 } muon_status;
 
 typedef enum muon_dtype { MUON_BF16 = 1, MUON_F32 = 2 } muon_dtype;

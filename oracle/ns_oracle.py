@@ -21,7 +21,7 @@ Sources (the pages are AI-written summaries of two papers):
   Newton-Schulz update runs locally on the rank that owns the full 2D
   gradient; non-matrix tensors form a tail that keeps using standard AdamW.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 
 * The pages give no polynomial, coefficients or iteration count.  The odd
   quintic X <- aX + b(XX^T)X + c(XX^T)^2X is used, with (a, b, c) and the step

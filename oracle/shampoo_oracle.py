@@ -8,7 +8,7 @@ Sources.  The MatrixFSDP summaries ("Resumen Técnico: MatrixFSDP", key contribu
 "기술 요약: MatrixFSDP", key contributions, generality) state that the owner-centric
 placement works unchanged for Muon, Shampoo and SOAP, because each needs the full 2D
 gradient on one rank, and that no distributed variant of the preconditioners is needed.  The
-pages do not define Shampoo.  The readings below (also listed in the design doc) take the plainest
+pages do not define Shampoo.  The readings below take the plainest
 form of the published method, Shampoo for a matrix parameter (Gupta, Koren and Singer, 2018),
 with its inverse roots computed by the coupled Newton iteration for inverse p-th roots (Guo and
 Higham, 2006), which needs only matrix products:
