@@ -12,8 +12,8 @@
  * fourth root computed by the coupled Newton iteration for inverse p-th roots (Guo and
  * Higham, 2006), which needs only matrix products.
  *
- * What is computed, per matrix W (rows x cols, fp32) with gradient G and statistics L
- * (rows x rows) and R (cols x cols):
+ * What is computed, per matrix W (rows x cols, fp32 or bf16) with gradient G (same dtype) and
+ * fp32 statistics L (rows x rows) and R (cols x cols):
  *   1. L <- beta2 L + G G^T,  R <- beta2 R + G^T G           (statistics, in place)
  *   2. for S in {L, R}: A = S + eps I, nu = ||S||_F + eps (>= the largest eigenvalue of A);
  *      X_0 = nu^(-1/4) I, M_0 = A / nu, and root_iters times
@@ -24,8 +24,9 @@
  * lower-triangle tiles and mirrored on store, as in muon_step.  The statistics of all
  * matrices share each launch.
  *
- * Precision: fp32 storage of every matrix and iterate, fp32 MFMA products (fp32 inputs,
- * fp32 accumulation).  A statistic's eigenvalues below about 1e-7 of its largest are not
+ * Precision: fp32 statistics, copies of G and iterates; fp32 MFMA products (fp32 inputs, fp32
+ * accumulation).  A bf16 W and G are read as bf16 (G is widened to fp32 exactly) and W' is
+ * rounded to bf16 (round to nearest even) from the fp32 update.  A statistic's eigenvalues below about 1e-7 of its largest are not
  * resolved in fp32, so directions that weak get a root with a large relative error when
  * eps is that small (this is the arithmetic, not the kernels: a float32 run of the same
  * iteration on the CPU shows it too).
@@ -44,8 +45,9 @@ extern "C" {
 #endif
 
 /* One owned matrix: param, stat_left and stat_right are updated in place, grad is read only.
- * param and grad are rows x cols, stat_left rows x rows, stat_right cols x cols; all fp32,
- * row-major, contiguous, 4-byte aligned device pointers, 1 <= rows, cols <= 65536. */
+ * param and grad are rows x cols of `dtype`; stat_left (rows x rows) and stat_right
+ * (cols x cols) are fp32; all row-major, contiguous device pointers aligned to their element
+ * size, 1 <= rows, cols <= 65536.  Matrices of both dtypes may be mixed in one call. */
 typedef struct shampoo_matrix {
   void* param;
   const void* grad;
@@ -53,7 +55,7 @@ typedef struct shampoo_matrix {
   void* stat_right;
   int64_t rows;
   int64_t cols;
-  int32_t dtype;    /* MUON_F32 (the only dtype) */
+  int32_t dtype;    /* MUON_F32 or MUON_BF16: the dtype of param and grad */
   int32_t reserved; /* must be 0 */
 } shampoo_matrix;
 

@@ -409,8 +409,9 @@ def make_shampoo_hparams(lr=0.01, beta2=1.0, eps=1e-6, root_iters=20) -> shampoo
 
 
 def shampoo_matrix_array(params, grads, lefts, rights):
-    """Pack lists of fp32 device tensors into a ctypes shampoo_matrix array: param and grad
-    rows x cols, left statistic rows x rows, right statistic cols x cols."""
+    """Pack lists of device tensors into a ctypes shampoo_matrix array: param and grad rows x cols
+    (float32, or bfloat16 for both), left statistic rows x rows and right statistic cols x cols
+    (float32)."""
     import torch
 
     if not (len(params) == len(grads) == len(lefts) == len(rights)):
@@ -422,20 +423,26 @@ def shampoo_matrix_array(params, grads, lefts, rights):
         for name, (t, shape) in want.items():
             if t.dim() != 2 or not t.is_contiguous() or tuple(t.shape) != shape:
                 raise ValueError(f"matrix {i}: {name} must be a contiguous {shape[0]} x {shape[1]} tensor")
-            if t.dtype != torch.float32:
-                raise TypeError(f"matrix {i}: {name} must be float32")
-        arr[i] = shampoo_matrix(w.data_ptr(), g.data_ptr(), lt.data_ptr(), rt.data_ptr(), r, c, MUON_F32, 0)
+        if g.dtype != w.dtype:
+            raise TypeError(f"matrix {i}: param and grad must have the same dtype")
+        if lt.dtype != torch.float32 or rt.dtype != torch.float32:
+            raise TypeError(f"matrix {i}: the statistics must be float32")
+        arr[i] = shampoo_matrix(w.data_ptr(), g.data_ptr(), lt.data_ptr(), rt.data_ptr(), r, c,
+                                _dtype_code(w), 0)
     return arr
 
 
-def shampoo_shape_array(shapes):
-    """A shampoo_matrix array with fake, distinct, aligned pointers: for host-only planning calls."""
+def shampoo_shape_array(shapes, dtype=MUON_F32):
+    """A shampoo_matrix array with fake, distinct, aligned pointers: for host-only planning calls.
+    A shape may carry a third entry, its dtype."""
     arr = (shampoo_matrix * max(1, len(shapes)))()
     base = 1 << 40
     page = lambda n: ((n * 4 + 4095) // 4096) * 4096  # noqa: E731
-    for i, (r, c) in enumerate(shapes):
+    for i, sh in enumerate(shapes):
+        r, c = sh[0], sh[1]
+        dt = sh[2] if len(sh) > 2 else dtype
         w, g, lt, rt = base, base + page(r * c), base + 2 * page(r * c), base + 2 * page(r * c) + page(r * r)
-        arr[i] = shampoo_matrix(w, g, lt, rt, r, c, MUON_F32, 0)
+        arr[i] = shampoo_matrix(w, g, lt, rt, r, c, dt, 0)
         base = rt + page(c * c)
     return arr
 

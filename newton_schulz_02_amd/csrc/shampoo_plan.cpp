@@ -204,8 +204,8 @@ int build_shampoo_plan(const shampoo_matrix* mats, int32_t count, const shampoo_
       *err = buf;
       return MUON_EINVAL;
     }
-    if (x.dtype != MUON_F32) {
-      snprintf(buf, sizeof buf, "matrix %d: dtype %d is not MUON_F32", i, x.dtype);
+    if (x.dtype != MUON_F32 && x.dtype != MUON_BF16) {
+      snprintf(buf, sizeof buf, "matrix %d: unknown dtype %d", i, x.dtype);
       *err = buf;
       return MUON_EINVAL;
     }
@@ -216,16 +216,15 @@ int build_shampoo_plan(const shampoo_matrix* mats, int32_t count, const shampoo_
     }
     const uintptr_t ptrs[4] = {(uintptr_t)x.param, (uintptr_t)x.grad, (uintptr_t)x.stat_left,
                                (uintptr_t)x.stat_right};
-    for (uintptr_t p : ptrs) {
-      if (p % 4) {
-        snprintf(buf, sizeof buf, "matrix %d: pointer not 4-byte aligned", i);
-        *err = buf;
-        return MUON_EINVAL;
-      }
+    const uintptr_t es = x.dtype == MUON_BF16 ? 2 : 4;  // param and grad; statistics are fp32
+    if (ptrs[0] % es || ptrs[1] % es || ptrs[2] % 4 || ptrs[3] % 4) {
+      snprintf(buf, sizeof buf, "matrix %d: pointer not aligned to its element size", i);
+      *err = buf;
+      return MUON_EINVAL;
     }
     const uintptr_t r = uintptr_t(x.rows), c = uintptr_t(x.cols);
-    spans.push_back({ptrs[0], ptrs[0] + r * c * 4, i, true});
-    spans.push_back({ptrs[1], ptrs[1] + r * c * 4, i, false});
+    spans.push_back({ptrs[0], ptrs[0] + r * c * es, i, true});
+    spans.push_back({ptrs[1], ptrs[1] + r * c * es, i, false});
     spans.push_back({ptrs[2], ptrs[2] + r * r * 4, i, true});
     spans.push_back({ptrs[3], ptrs[3] + c * c * 4, i, true});
   }
@@ -292,8 +291,10 @@ int build_shampoo_plan(const shampoo_matrix* mats, int32_t count, const shampoo_
     p.n = std::max(p.r, p.c);
     p.mp = round_up(p.r, kKPad);  // padded rows (the contraction of X_L G)
     p.np = round_up(p.c, kKPad);  // padded cols (the contraction of Z X_R)
-    p.dtype = p.gdtype = kF32;
-    p.esize = p.gsize = 4;
+    p.dtype = mats[i].dtype == MUON_BF16 ? int(kBF16) : int(kF32);  // W and G
+    p.esize = p.dtype == kBF16 ? 2 : 4;
+    p.gdtype = kF32;  // the copies of G, the products and the statistics
+    p.gsize = 4;
     p.full_tiles = full_tiles(p.r, p.c);
     p.full_prefix = full;
     full += p.full_tiles;
@@ -307,8 +308,8 @@ int build_shampoo_plan(const shampoo_matrix* mats, int32_t count, const shampoo_
     p.flops = double(p.r) * double(p.r + 1) * double(p.c) + double(p.c) * double(p.c + 1) * double(p.r) +
               2.0 * double(p.r) * double(p.r) * double(p.c) + 2.0 * double(p.r) * double(p.c) * double(p.c);
     // Compulsory HBM bytes: read G, read and write W and both statistics.
-    p.bytes = 4.0 * (3.0 * double(p.r) * double(p.c) + 2.0 * double(p.r) * double(p.r) +
-                     2.0 * double(p.c) * double(p.c));
+    p.bytes = 3.0 * double(p.esize) * double(p.r) * double(p.c) +
+              4.0 * (2.0 * double(p.r) * double(p.r) + 2.0 * double(p.c) * double(p.c));
     plan.flops += p.flops;
     plan.bytes += p.bytes;
   }
@@ -449,17 +450,23 @@ int build_shampoo_plan(const shampoo_matrix* mats, int32_t count, const shampoo_
     return int8_t(slot[size_t(v)]);
   };
   const int sfirst = count, slast = int(entries);
-  {  // copies of G and G^T (the momentum kernel with no momentum buffer)
+  // Copies of G and G^T in fp32 (the momentum kernel with no momentum buffer), one launch per
+  // run of matrices of one dtype.
+  for (int f = 0; f < count;) {
+    int l = f;
+    while (l < count && plan.mats[size_t(l)].dtype == plan.mats[size_t(f)].dtype) ++l;
     PlanLaunch L;
     L.kind = kLaunchMomentum;
-    L.dtype = kF32;
-    L.first = 0;
-    L.last = count;
-    for (int i = 0; i < count; ++i) {
-      L.tiles += plan.mats[size_t(i)].mom_tiles;
-      L.bytes += 12.0 * double(plan.mats[size_t(i)].r) * double(plan.mats[size_t(i)].c);
+    L.dtype = plan.mats[size_t(f)].dtype;
+    L.first = f;
+    L.last = l;
+    for (int i = f; i < l; ++i) {
+      const PlanMat& p = plan.mats[size_t(i)];
+      L.tiles += p.mom_tiles;
+      L.bytes += (double(p.esize) + 8.0) * double(p.r) * double(p.c);
     }
     plan.launches.push_back(L);
+    f = l;
   }
   {
     PlanLaunch L;
@@ -612,8 +619,12 @@ void fill_shampoo_descs(const ShampooPlan& sp, const shampoo_matrix* mats,
     d.trans_ld = p.mp;
     d.rows = int32_t(p.r);
     d.cols = int32_t(p.c);
-    d.vec = ((uintptr_t)x.grad % 16 == 0 && (p.c * 4) % 16 == 0) ? 1 : 0;
-    d.wvec = ((uintptr_t)x.param % 16 == 0 && (p.c * 4) % 16 == 0) ? 1 : 0;
+    const int64_t es = int64_t(p.esize);
+    d.vec = ((uintptr_t)x.grad % 16 == 0 && (p.c * es) % 16 == 0) ? 1 : 0;
+    d.wvec = ((uintptr_t)x.param % 16 == 0 && (p.c * es) % 16 == 0) ? 1 : 0;
+    // bf16 W and G: the momentum kernel writes fp32 copies of G, and the fp32 kernel's update
+    // rounds W to bf16.
+    d.gram_f32 = p.dtype == kBF16 ? 1 : 0;
     d.buf[kShG] = {g, p.np, int32_t(p.r), int32_t(p.np)};
     d.buf[kShGT] = {gt, p.mp, int32_t(p.c), int32_t(p.mp)};
     d.buf[kShXL] = slot_desc(sp.left_entry[size_t(i)], sp.root_slot);
@@ -670,7 +681,7 @@ std::string describe_shampoo_plan(const ShampooPlan& sp) {
     const PlanMat& p = plan.mats[e];
     const bool stat = int(e) >= sp.count;
     os << (e ? "," : "") << "{\"kind\":\"" << (stat ? (sp.stat_right[e - size_t(sp.count)] ? "right" : "left") : "grad")
-       << "\",\"matrix\":" << p.orig << ",\"rows\":" << p.r << ",\"cols\":" << p.c << ",\"m\":" << p.m
+       << "\",\"dtype\":" << p.dtype << ",\"matrix\":" << p.orig << ",\"rows\":" << p.r << ",\"cols\":" << p.c << ",\"m\":" << p.m
        << ",\"tiles\":" << (stat ? p.tri_tiles : p.full_tiles) << ",\"mom_tiles\":" << p.mom_tiles
        << ",\"regions\":[";
     bool first = true;

@@ -28,11 +28,20 @@ STAT_TOL = 1e-5
 UPD_TOL = 1e-4
 
 
-def _run(shapes, seed, *, stats="warm", iters=5, beta2=0.9, eps=None, lr=0.05, steps=1, grad_std=1e-2):
+def _run(shapes, seed, *, stats="warm", iters=5, beta2=0.9, eps=None, lr=0.05, steps=1, grad_std=1e-2,
+         dtypes=None):
     """Run `steps` Shampoo steps on the GPU (a fresh gradient each step after the first) and the
-    oracle on the same inputs; return the worst relative errors (update, statistics)."""
-    log(f"shampoo shapes={shapes} seed={seed} stats={stats} iters={iters} beta2={beta2} steps={steps}")
+    oracle on the same inputs; return the worst relative errors (update, statistics).  dtypes:
+    per matrix torch.float32 (default) or torch.bfloat16 for W and G (the oracle gets the
+    same rounded values)."""
+    log(f"shampoo shapes={shapes} seed={seed} stats={stats} iters={iters} beta2={beta2} steps={steps}"
+        f" dtypes={dtypes}")
     items = list(W.shampoo_inputs(shapes, seed, stats=stats, grad_std=grad_std))
+    dtypes = dtypes or [torch.float32] * len(shapes)
+    # bf16 W starts at zero, as in the Muon parity runs: W' is then the update rounded once to
+    # bf16, and the comparison measures the update rather than the rounding of a large W.
+    items = [((w.to(dt) if dt == torch.float32 else torch.zeros_like(w, dtype=dt)), g.to(dt), lt, rt)
+             for (w, g, lt, rt), dt in zip(items, dtypes)]
     if eps is None:
         eps = 1e-2 * grad_std ** 2 * max(max(s) for s in shapes) if stats == "zero" else 1e-6
     Ws = [w.to(DEV) for w, _, _, _ in items]
@@ -47,6 +56,7 @@ def _run(shapes, seed, *, stats="warm", iters=5, beta2=0.9, eps=None, lr=0.05, s
         if k > 0:  # new gradients, written in place so the prepared step sees them
             for i, g in enumerate(Gs):
                 new = torch.from_numpy((rng.standard_normal(tuple(g.shape)) * grad_std).astype(np.float32))
+                new = new.to(g.dtype)
                 g.copy_(new)
                 ref[i][1] = new.double().numpy()
         W_before = [to64(w) for w in Ws]
@@ -139,3 +149,23 @@ def test_workspace_too_small():
         nm.shampoo_step_raw(step.arr, 1, step.hp, step.workspace.data_ptr(), step.ws_bytes - 256,
                             nm._stream_handle(None, step.device))
     assert ei.value.status == nm.MUON_ENOSPC
+
+
+BF16_TOL = 2e-2  # bf16 W and G: the bar of bf16 inputs
+
+
+@pytest.mark.parametrize("shapes", [[(200, 300)], [(513, 129)], [(96, 96), (257, 130), (64, 700)]], ids=str)
+def test_bf16_parameters(shapes):
+    """bf16 W and G with fp32 statistics; the update is rounded once to bf16."""
+    upd, stat = _run(shapes, seed=81 + len(shapes), iters=8, dtypes=[torch.bfloat16] * len(shapes))
+    assert stat <= STAT_TOL and upd <= BF16_TOL
+
+
+def test_mixed_dtypes_in_one_call():
+    shapes = [(200, 300), (128, 256), (300, 200), (64, 64)]
+    dts = [torch.bfloat16, torch.float32, torch.bfloat16, torch.float32]
+    upd, stat = _run(shapes, seed=91, iters=6, dtypes=dts)
+    assert stat <= STAT_TOL and upd <= BF16_TOL
+    # the fp32 matrices alone keep the fp32 bar
+    upd32, _ = _run([shapes[1], shapes[3]], seed=91, iters=6)
+    assert upd32 <= UPD_TOL

@@ -217,7 +217,8 @@ def test_bad_hparams(field, value):
 def test_bad_matrices():
     hp = nm.make_shampoo_hparams()
     for mutate in (lambda m: setattr(m, "rows", 0), lambda m: setattr(m, "cols", 65537),
-                   lambda m: setattr(m, "dtype", nm.MUON_BF16), lambda m: setattr(m, "reserved", 1),
+                   lambda m: setattr(m, "dtype", 3), lambda m: setattr(m, "reserved", 1),
+                   lambda m: setattr(m, "stat_right", m.stat_right + 2),
                    lambda m: setattr(m, "stat_left", None), lambda m: setattr(m, "grad", m.grad + 2)):
         arr = nm.shampoo_shape_array([(8, 8)])
         mutate(arr[0])
@@ -284,3 +285,22 @@ def test_tail_split_of_the_statistics():
     finally:
         nm.tune_force(None)
     assert nm.shampoo_workspace_size_raw(arr, 4, hp) == plan["workspace"]
+
+
+def test_bf16_matrices():
+    """bf16 W and G: accepted (2-byte alignment), copied to fp32 by one momentum launch per run
+    of one dtype, mixed with fp32 matrices in one call."""
+    hp = nm.make_shampoo_hparams(root_iters=3)
+    arr = nm.shampoo_shape_array([(64, 96, nm.MUON_BF16), (64, 96, nm.MUON_BF16), (32, 48), (16, 16, nm.MUON_BF16)])
+    arr[0].grad += 2  # 2-byte aligned is enough for bf16
+    plan = nm.shampoo_plan_describe(arr, 4, hp)
+    moms = [(L["first"], L["last"]) for L in plan["launches"] if L["kind"] == "momentum"][:-1]
+    assert moms == [(0, 2), (2, 3), (3, 4)]
+    assert [e["dtype"] for e in plan["entries"][:4]] == [1, 1, 2, 1]
+    assert all(e["dtype"] == 2 for e in plan["entries"][4:])  # statistics are fp32
+    bad = nm.shampoo_shape_array([(8, 8, nm.MUON_BF16)])
+    bad[0].grad += 1
+    assert _status(bad, 1, hp) == nm.MUON_EINVAL
+    bad = nm.shampoo_shape_array([(8, 8, nm.MUON_BF16)])
+    bad[0].stat_left += 2  # statistics need 4-byte alignment
+    assert _status(bad, 1, hp) == nm.MUON_EINVAL
