@@ -82,6 +82,22 @@ def traffic_from_profiles(kernel: str, workload: str, launches: list[tuple[int, 
     return total / len(launches)
 
 
+def shampoo_traffic_from_profile(workload: str):
+    """Mean HBM bytes per fp32 MFMA launch of a Shampoo step, from the committed counter summary
+    ``profiles/gemm_<workload>_hbm_traffic.md``, or None when it is missing or the kernel sources
+    changed since it was taken."""
+    path = ROOT / "profiles" / f"gemm_{workload}_hbm_traffic.md"
+    if not path.exists():
+        return None
+    text = path.read_text()
+    m_hash = re.search(r"^kernel_hash gemm_f32:\s*([0-9a-f]+)", text, re.M)
+    m_bytes = re.search(r"^launch_bytes:\s*([0-9.eE+, ]+)$", text, re.M)
+    if not m_hash or m_hash.group(1) != kernel_hash("gemm_f32") or not m_bytes:
+        return None
+    vals = [float(x) for x in m_bytes.group(1).split(",")]
+    return sum(vals) / len(vals)
+
+
 def cpu_baseline(wl, budget_s: float = 30.0):
     """Time the CPU oracle on a bounded sample of the workload: its matrices in list order
     until about ``budget_s`` seconds have been spent (at least one matrix)."""
@@ -250,7 +266,7 @@ def bench_shampoo(args) -> int:
             "peak": F32_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / F32_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": shampoo_traffic_from_profile(wl.name) if args.kernel == "tuned" else None,
             "launches_per_step": gs["launches"] // args.steps,
             "avg_launch_ms": round(avg_ms, 5),
             "flops_per_launch": flops_per_launch,
