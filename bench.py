@@ -6,7 +6,9 @@ iterations, lr 0.02, beta 0.95.  One step = one muon_step over all seven matrice
 (momentum, normalisation, Gram Newton-Schulz and the update), inputs resident in HBM.
 
 Prints one JSON line:
-  value          algorithmic TFLOP/s of the whole step (symmetric products count m(m+1)k)
+  value          algorithmic TFLOP/s of the whole step (symmetric products count m(m+1)k), from
+                 the mean step time over the timed region (ms_per_step); ms_per_step_median and
+                 ms_per_step_min come from an event between consecutive steps
   roofline       the MFMA contraction kernel against the bf16 dense peak, its duration taken
                  from HIP events around each of its launches over the timed steps
   cpu_baseline   the float64 CPU oracle on a bounded sample of the same workload
@@ -80,6 +82,14 @@ def traffic_from_profiles(kernel: str, workload: str, launches: list[tuple[int, 
             return None
         total += per_launch[i]
     return total / len(launches)
+
+
+def step_times_ms(marks) -> dict:
+    """Median and minimum of the per-step times between consecutive events (ms)."""
+    import statistics
+
+    t = [a.elapsed_time(b) for a, b in zip(marks, marks[1:])]
+    return {"median": round(statistics.median(t), 4), "min": round(min(t), 4)} if t else {}
 
 
 def shampoo_traffic_from_profile(workload: str):
@@ -211,13 +221,17 @@ def bench_shampoo(args) -> int:
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     start.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step(stream)
+        marks[i + 1].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
     stats = nm.profile_end()
     ms = start.elapsed_time(stop) / args.steps
+    per_step = step_times_ms(marks)
     value = flops / (ms * 1e-3) / 1e12
     gs = stats["gemm_f32"]
     avg_ms = gs["ms"] / gs["launches"]
@@ -240,6 +254,8 @@ def bench_shampoo(args) -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": per_step.get("median"),
+        "ms_per_step_min": per_step.get("min"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -383,13 +399,17 @@ def main() -> int:
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     start.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         one_step()
+        marks[i + 1].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
     stats = nm.profile_end()
     ms = start.elapsed_time(stop) / args.steps
+    per_step = step_times_ms(marks)
 
     value = flops / (ms * 1e-3) / 1e12
     # The dominant MFMA kernel: the one with the most time in the timed steps.
@@ -422,6 +442,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": per_step.get("median"),
+        "ms_per_step_min": per_step.get("min"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
