@@ -34,6 +34,8 @@
  *   - No C++ exception crosses the ABI.  Status codes are muon_status values.
  *   - The library allocates no device memory.  It keeps a small pinned host staging ring
  *     for launch descriptors, released by muon_shutdown().
+ *   - Calls may come from several host threads and go to several streams at once, each
+ *     with its own workspace; results do not depend on how they interleave.
  */
 #ifndef MUON_H
 #define MUON_H
