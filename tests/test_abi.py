@@ -310,3 +310,31 @@ def test_xcd_remap_is_a_permutation_dealing_chunks_round_robin(total):
         assert len(blk) in (rest // 8, -(-rest // 8))
         start += len(blk)
     assert start == total
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every entry point raises; nothing falls back to the CPU."""
+    import torch
+
+    monkeypatch.setattr(nm, "LIB_PATH", tmp_path / "libmuon.so")
+    monkeypatch.setattr(nm, "_lib", None)
+    with pytest.raises(nm.MuonLibraryMissing):
+        nm.lib()
+    w = torch.zeros(8, 16, dtype=torch.bfloat16)
+    with pytest.raises(nm.MuonLibraryMissing):
+        nm.MuonStep([w], [w.clone()], [w.clone()], lr=0.02, beta=0.95)
+    f = torch.zeros(8, 16)
+    with pytest.raises(nm.MuonLibraryMissing):
+        nm.ShampooStep([f], [f.clone()], [torch.zeros(8, 8)], [torch.zeros(16, 16)], lr=0.1,
+                       beta2=0.9, eps=1e-6, root_iters=4)
+
+
+def test_product_code_never_reaches_the_oracle():
+    """The package and the C sources name no oracle module: the oracle only checks results."""
+    root = Path(nm.__file__).resolve().parent
+    files = list(root.glob("*.py")) + list((root / "csrc").glob("*"))
+    for f in files:
+        if f.is_file() and f.suffix in (".py", ".cpp", ".h", ".hip"):
+            text = f.read_text()
+            assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
+            assert "oracle/" not in text, f
