@@ -353,6 +353,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
       issue(ks + kStages - 1, stage_of(std::integral_constant<int, decltype(sc)::value + kStages - 1>{}));
     if (idle) return;
     const char* st = stage_of(sc);
+    // Scheduling hint for this MFMA block: the compiler then issues the stage's fragment
+    // reads early, one between consecutive MFMAs, instead of four or two ahead of each
+    // group with a wait on each; measured 2-3 % faster per step, no spills.
+    __builtin_amdgcn_iglp_opt(1);
 #pragma unroll
     for (int kk = 0; kk < kKK; ++kk) {
       uint4 fa[4], fb[kFragN];
