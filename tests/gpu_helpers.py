@@ -29,8 +29,12 @@ def relf(a: np.ndarray, b: np.ndarray) -> float:
     return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a))
 
 
-def run_gpu(wl: W.Workload, weights: str = "zeros", steps=None, restart_mask=nm.RESTART_AUTO):
-    """Draw inputs, run one muon_step on the GPU; return host copies (inputs and outputs)."""
+def run_gpu(wl: W.Workload, weights: str = "zeros", steps=None, restart_mask=nm.RESTART_AUTO,
+            tune_reps: int = 0):
+    """Draw inputs, run one muon_step on the GPU; return host copies (inputs and outputs).
+
+    tune_reps > 0 first picks each launch's kernel configuration by timing (muon_tune on
+    copies of the inputs, as bench.py does at set-up); the step then runs with that table."""
     items = list(W.generate(wl, weights=weights))
     params = [w.to(DEV) for _, w, _, _ in items]
     grads = [g.to(DEV) for _, _, g, _ in items]
@@ -38,6 +42,8 @@ def run_gpu(wl: W.Workload, weights: str = "zeros", steps=None, restart_mask=nm.
     step = nm.MuonStep(params, grads, moms, lr=wl.lr, beta=wl.beta, coeffs=wl.coeffs,
                        steps=wl.steps if steps is None else steps, eps=wl.eps,
                        restart_mask=restart_mask)
+    if tune_reps > 0:
+        step.tune(reps=tune_reps)
     step()
     torch.cuda.synchronize()
     return {

@@ -121,6 +121,33 @@ def test_layer4096_full_size():
         assert momentum_ok(res["M0"][i], res["G"][i], res["M1"][i], wl.beta, spec.dtype), spec.name
 
 
+def test_layer4096_full_size_tuned():
+    """The benchmarked workload at its real size with the kernel configuration per launch
+    chosen by timing, as the bench chooses it (a mix of 256 x 256 and 256 x 384 tiles with
+    and without the tail split): W' for a square and the tall matrix, momentum for all."""
+    wl = W.WORKLOADS["layer4096_bf16"]
+    nm.tune_clear()
+    nm.tune_force(None)
+    try:
+        log(f"case {wl.name} tuned")
+        res = run_gpu(wl, tune_reps=3)
+        table = nm.tune_table()
+        log("tuned configurations: " + " ".join(str(v) for v in table.values()))
+        arr = nm.shape_array([(s.rows, s.cols) for s in wl.matrices])
+        hp = nm.make_hparams(lr=wl.lr, beta=wl.beta, coeffs=wl.coeffs, steps=wl.steps, eps=wl.eps)
+        d = nm.plan_describe(arr, wl.count, hp)
+        gemms = [L for L in d["launches"] if L["kind"] == "gemm"]
+        assert len(gemms) == 16 and all(L["signature"] in table for L in gemms)
+        names = [s.name for s in res["specs"]]
+        for i in (names.index("q"), names.index("down")):
+            check_matrix(res, i, wl)
+        for i, spec in enumerate(res["specs"]):
+            assert momentum_ok(res["M0"][i], res["G"][i], res["M1"][i], wl.beta, spec.dtype), spec.name
+    finally:
+        nm.tune_force(None)
+        nm.tune_clear()
+
+
 def test_owner_share_full_size():
     """One owner's 28 matrices and its packed AdamW tail at their real sizes, launched as the
     bench launches them: one muon_step over all 28, then adamw_step on the same stream.
