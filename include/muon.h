@@ -194,8 +194,9 @@ int muon_plan_describe(const muon_matrix* mats, int32_t count, const muon_hparam
                        size_t len);
 
 /* Per-kernel timing.  Between muon_profile_begin() and muon_profile_end(), each launch made
- * by muon_step()/adamw_step() is bracketed by HIP events on its stream.  muon_profile_end()
- * waits for those events and writes one record per kernel kind. */
+ * by muon_step()/adamw_step() is bracketed by HIP events on its stream.  The events serve
+ * timing only and carry no system-scope memory fence.  muon_profile_end() waits for them and
+ * writes one record per kernel kind. */
 typedef struct muon_kernel_stat {
   char name[32];
   int64_t launches;
