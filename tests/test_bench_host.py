@@ -1,0 +1,63 @@
+"""Host logic of bench.py (no GPU): the one-GPU guard, the traffic figures taken from the
+committed counter summaries and withheld once a kernel's sources change, and the step-time
+statistics."""
+
+from __future__ import annotations
+
+import subprocess
+import sys
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+sys.path.insert(0, str(ROOT))
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_traffic_follows_the_summary_while_the_hash_matches():
+    text = (ROOT / "profiles" / "gemm_layer4096_bf16_hbm_traffic.md").read_text()
+    rows = {c: [float(x) for x in text.split(f"launch_bytes cfg{c}:")[1].splitlines()[0].split(",")]
+            for c in range(4)}
+    assert all(len(v) == 16 for v in rows.values())
+    launches = [(0, 0), (5, 2), (15, 0)]
+    want = (rows[0][0] + rows[2][5] + rows[0][15]) / 3
+    got = bench.traffic_from_profiles("gemm_bf16", "layer4096_bf16", launches)
+    assert got == pytest.approx(want, rel=1e-12)
+    assert bench.traffic_from_profiles("gemm_bf16", "layer4096_bf16", []) is None
+    assert bench.traffic_from_profiles("gemm_bf16", "no_such_workload", launches) is None
+
+
+def test_traffic_is_withheld_when_the_kernel_changed(monkeypatch):
+    monkeypatch.setattr(bench, "kernel_hash", lambda kernel="gemm_bf16": "0" * 16)
+    assert bench.traffic_from_profiles("gemm_bf16", "layer4096_bf16", [(0, 0)]) is None
+    assert bench.shampoo_traffic_from_profile("shampoo_layer4096_f32") is None
+
+
+def test_shampoo_traffic_is_the_mean_per_launch():
+    text = (ROOT / "profiles" / "gemm_shampoo_layer4096_f32_hbm_traffic.md").read_text()
+    line = [l for l in text.splitlines() if l.startswith("launch_bytes:")][0]
+    vals = [float(x) for x in line.split(":", 1)[1].split(",")]
+    assert bench.shampoo_traffic_from_profile("shampoo_layer4096_f32") == pytest.approx(
+        sum(vals) / len(vals), rel=1e-12)
+
+
+class _Mark:
+    def __init__(self, t):
+        self.t = t
+
+    def elapsed_time(self, other):
+        return other.t - self.t
+
+
+def test_step_times_median_and_min():
+    marks = [_Mark(t) for t in (0.0, 10.5, 21.3, 31.6, 43.0)]   # steps 10.5, 10.8, 10.3, 11.4
+    st = bench.step_times_ms(marks)
+    assert st["median"] == pytest.approx(10.65) and st["min"] == pytest.approx(10.3)
+    assert bench.step_times_ms(marks[:1]) == {}
