@@ -364,3 +364,31 @@ def test_profile_reports_each_kernel():
     assert stats["momentum_bf16"]["launches"] == 1 and stats["norm"]["launches"] == 1
     assert stats["gemm_bf16"]["launches"] >= 15
     assert stats["gemm_bf16"]["ms"] > 0 and stats["gemm_bf16"]["flops"] > 0
+
+
+def test_profile_times_fit_inside_the_step():
+    """The per-launch event times (fence-free timing events) add up to most of the step's
+    wall time and never exceed it."""
+    wl = W.custom("prof2", [(1024, 4096)] * 4, seed=15)
+    items = list(W.generate(wl, weights="random"))
+    params = [w.to(DEV) for _, w, _, _ in items]
+    grads = [g.to(DEV) for _, _, g, _ in items]
+    moms = [m.to(DEV) for _, _, _, m in items]
+    step = nm.MuonStep(params, grads, moms, lr=wl.lr, beta=wl.beta, coeffs=wl.coeffs,
+                       steps=wl.steps, eps=wl.eps)
+    stream = torch.cuda.current_stream()
+    step(stream)
+    torch.cuda.synchronize()
+    log("case profile times inside the step")
+    nm.profile_begin()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    step(stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    stats = nm.profile_end()
+    wall = a.elapsed_time(b)
+    total = sum(v["ms"] for v in stats.values())
+    log(f"  kernels {total:.4f} ms of a {wall:.4f} ms step")
+    assert 0.5 * wall < total <= 1.01 * wall + 0.005
