@@ -7,11 +7,14 @@ iterations, lr 0.02, beta 0.95.  One step = one muon_step over all seven matrice
 
 Prints one JSON line:
   value          algorithmic TFLOP/s of the whole step (symmetric products count m(m+1)k), from
-                 the mean step time over the timed region (ms_per_step); ms_per_step_median and
-                 ms_per_step_min come from an event between consecutive steps
+                 the mean step time over the timed region (ms_per_step), which holds only the
+                 steps and two bracketing events; ms_per_step_median and ms_per_step_min come
+                 from a second pass of as many steps with an event between consecutive steps,
+                 and matrices_per_s is the matrix count over that median
   roofline       the MFMA contraction kernel against the bf16 dense peak, its duration taken
-                 from HIP events around each of its launches over the timed steps
-  cpu_baseline   the float64 CPU oracle on a bounded sample of the same workload
+                 from HIP events around each of its launches in a third, instrumented pass
+  cpu_baseline   the float64 CPU oracle: every matrix of the one-matrix, 16-matrix and layer
+                 workloads; one matrix per shape, scaled by count, for the larger ones
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py --optimizer shampoo [--workload shampoo_layer4096_f32]
@@ -92,6 +95,38 @@ def step_times_ms(marks) -> dict:
     return {"median": round(statistics.median(t), 4), "min": round(min(t), 4)} if t else {}
 
 
+def timed_passes(one_step, steps: int, record, sync, profile_begin, profile_end, prof_steps: int = 5):
+    """Run the three measurement passes of a benchmark step.
+
+    1. ``steps`` steps bracketed by two events and nothing else: the mean step time (ms).
+    2. ``steps`` more with an event between consecutive steps: median and minimum step time.
+    3. ``min(steps, prof_steps)`` instrumented steps between ``profile_begin`` and
+       ``profile_end``: the per-kernel statistics.
+    ``record()`` returns a recorded event (with ``elapsed_time``), ``sync()`` waits for the
+    device.  Returns (mean_ms, {"median", "min"}, stats, instrumented step count).
+    """
+    sync()
+    start = record()
+    for _ in range(steps):
+        one_step()
+    stop = record()
+    sync()
+    mean_ms = start.elapsed_time(stop) / steps
+    marks = [record()]
+    for _ in range(steps):
+        one_step()
+        marks.append(record())
+    sync()
+    per_step = step_times_ms(marks)
+    n_prof = min(steps, prof_steps)
+    profile_begin()
+    for _ in range(n_prof):
+        one_step()
+    sync()
+    stats = profile_end()
+    return mean_ms, per_step, stats, n_prof
+
+
 def shampoo_traffic_from_profile(workload: str):
     """Mean HBM bytes per fp32 MFMA launch of a Shampoo step, from the committed counter summary
     ``profiles/gemm_<workload>_hbm_traffic.md``, or None when it is missing or the kernel sources
@@ -108,43 +143,77 @@ def shampoo_traffic_from_profile(workload: str):
     return sum(vals) / len(vals)
 
 
-def cpu_baseline(wl, budget_s: float = 30.0):
-    """Time the CPU oracle on a bounded sample of the workload: its matrices in list order
-    until about ``budget_s`` seconds have been spent (at least one matrix)."""
-    import numpy as np
+# Workloads whose oracle baseline is always timed on every matrix; the larger ones are timed
+# one matrix per shape and scaled by the shape's count ("extrapolated").
+FULL_BASELINE = {"single_f32_256x1024", "batch16_bf16_1024x4096", "layer4096_bf16"}
+
+
+def host_blas() -> dict:
+    """Host cores this process may use, and the BLAS library numpy calls with its thread count."""
+    cores = len(os.sched_getaffinity(0))
+    lib, threads = "unknown", None
+    try:
+        from threadpoolctl import threadpool_info
+
+        for d in threadpool_info():
+            if d.get("user_api") == "blas":
+                lib = f"{d.get('internal_api')} {d.get('version') or ''}".strip()
+                threads = int(d.get("num_threads", 1))
+                break
+    except Exception:
+        pass
+    return {"cores": cores, "blas": lib, "blas_threads": threads}
+
+
+def cpu_baseline(wl, full: bool | None = None):
+    """Time the CPU oracle on the workload.  ``full`` (default: the workload is in
+    FULL_BASELINE): every matrix, in list order.  Otherwise the first matrix of each distinct
+    (rows, cols, dtype) is timed and its time multiplied by that shape's count."""
     import torch
 
     from newton_schulz_02_amd import workloads as W
     from oracle import muon_step as oracle_step
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max((d.get("num_threads", 1) for d in threadpool_info()
-                       if d.get("user_api") == "blas"), default=1)
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    done, flops, spent = [], 0.0, 0.0
+    if full is None:
+        full = wl.name in FULL_BASELINE
+    counts: dict = {}
+    for spec in wl.matrices:
+        key = (spec.rows, spec.cols, spec.dtype)
+        counts[key] = counts.get(key, 0) + 1
+    timed: dict = {}
+    flops, spent, n_run = 0.0, 0.0, 0
     for spec, w, g, m in W.generate(wl, weights="random"):
-        if done and spent >= budget_s * 0.5:
-            break
+        key = (spec.rows, spec.cols, spec.dtype)
+        if not full and key in timed:
+            continue
         w64, g64, m64 = (t.to(torch.float64).numpy() for t in (w, g, m))
         t0 = time.perf_counter()
         oracle_step(w64, g64, m64, lr=wl.lr, beta=wl.beta, coeffs=wl.coeffs, steps=wl.steps, eps=wl.eps)
-        spent += time.perf_counter() - t0
+        dt = time.perf_counter() - t0
+        n_run += 1
         mm, nn = min(spec.rows, spec.cols), max(spec.rows, spec.cols)
-        flops += algorithmic_flops_one(mm, nn, wl)
-        done.append(f"{spec.name} {spec.rows}x{spec.cols}")
-        if spent >= budget_s:
-            break
+        f = algorithmic_flops_one(mm, nn, wl)
+        scale = 1 if full else counts[key]
+        spent += dt * scale
+        flops += f * scale
+        timed[key] = dt
+    host = host_blas()
+    if full:
+        sample = f"float64 direct Newton-Schulz oracle on all {n_run} matrices, {spent:.1f} s"
+    else:
+        sample = (f"extrapolated: float64 direct Newton-Schulz oracle timed on one matrix of each of the "
+                  f"{len(timed)} shapes ({', '.join(f'{r}x{c} x{counts[(r, c, d)]}' for r, c, d in timed)}), "
+                  f"scaled by count to {spent:.1f} s for the {wl.count} matrices")
     return {
         "value": flops / spent / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": host["cores"],
         "kind": "oracle",
-        "sample": f"float64 direct Newton-Schulz oracle on {len(done)} of {wl.count} matrices "
-                  f"({', '.join(done)}), {spent:.1f} s; flops counted with the same rule as value",
+        "sample": sample + "; flops counted with the same rule as value",
         "seconds": spent,
+        "blas": host["blas"],
+        "blas_threads": host["blas_threads"],
+        "extrapolated": not full,
     }
 
 
@@ -156,13 +225,7 @@ def cpu_baseline_shampoo(wl, budget_s: float = 30.0):
 
     from oracle.shampoo_oracle import inverse_root_newton, root_scale
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max((d.get("num_threads", 1) for d in threadpool_info()
-                       if d.get("user_api") == "blas"), default=1)
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    host = host_blas()
     _, _, L0, _ = next(iter(wl.generate()))
     A = L0.double().numpy() + wl.eps * np.eye(L0.shape[0])
     nu = root_scale(L0.double().numpy(), wl.eps)
@@ -178,7 +241,9 @@ def cpu_baseline_shampoo(wl, budget_s: float = 30.0):
     return {
         "value": flops / spent / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": host["cores"],
+        "blas": host["blas"],
+        "blas_threads": host["blas_threads"],
         "kind": "oracle",
         "sample": f"float64 coupled-Newton inverse fourth root of one {m}x{m} statistic, {iters} of "
                   f"{wl.root_iters} steps, {spent:.1f} s; flops counted with the same rule as value",
@@ -217,27 +282,19 @@ def bench_shampoo(args) -> int:
         step(stream)
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
-    nm.profile_begin()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    start.record(stream)
-    marks[0].record(stream)
-    for i in range(args.steps):
-        step(stream)
-        marks[i + 1].record(stream)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    stats = nm.profile_end()
-    ms = start.elapsed_time(stop) / args.steps
-    per_step = step_times_ms(marks)
+    def record():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    ms, per_step, stats, prof_steps = timed_passes(lambda: step(stream), args.steps, record,
+                                                   torch.cuda.synchronize, nm.profile_begin, nm.profile_end)
     value = flops / (ms * 1e-3) / 1e12
     gs = stats["gemm_f32"]
     avg_ms = gs["ms"] / gs["launches"]
     flops_per_launch = gs["flops"] / gs["launches"]
     achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
-    kernels = {k: {"launches": v["launches"] // args.steps, "ms_per_step": v["ms"] / args.steps,
+    kernels = {k: {"launches": v["launches"] // prof_steps, "ms_per_step": v["ms"] / prof_steps,
                    "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None,
                    "gbs": (v["bytes"] / (v["ms"] * 1e-3) / 1e9) if v["bytes"] else None}
                for k, v in stats.items()}
@@ -261,7 +318,7 @@ def bench_shampoo(args) -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "matrices_per_s": round(wl.count / (ms * 1e-3), 3),
+        "matrices_per_s": round(wl.count / (per_step["median"] * 1e-3), 3) if per_step else None,
         "pct_of_f32_peak": round(100.0 * value / F32_PEAK_TFLOPS, 2),
         "algorithmic_flops_per_step": flops,
         "config": {
@@ -283,9 +340,10 @@ def bench_shampoo(args) -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / F32_PEAK_TFLOPS, 4),
             "traffic": shampoo_traffic_from_profile(wl.name) if args.kernel == "tuned" else None,
-            "launches_per_step": gs["launches"] // args.steps,
+            "launches_per_step": gs["launches"] // prof_steps,
             "avg_launch_ms": round(avg_ms, 5),
             "flops_per_launch": flops_per_launch,
+            "timing": f"HIP events around each launch over {prof_steps} profiled steps after the timed ones",
         },
         "kernels": kernels,
         "cpu_baseline": cpu,
@@ -323,7 +381,7 @@ def main() -> int:
     ap.add_argument("--optimizer", choices=["muon", "shampoo"], default="muon")
     ap.add_argument("--workload", default="layer4096_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=30.0)
+    ap.add_argument("--cpu-budget", type=float, default=30.0, help="Shampoo oracle sample only")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--kernel", choices=["tuned", "square", "wide", "square-split", "wide-split"],
                     default="tuned",
@@ -394,22 +452,17 @@ def main() -> int:
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
 
-    # Timed region: per-launch HIP events (on the launch stream) give the kernel durations.
-    nm.profile_begin()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    start.record(stream)
-    marks[0].record(stream)
-    for i in range(args.steps):
-        one_step()
-        marks[i + 1].record(stream)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    stats = nm.profile_end()
-    ms = start.elapsed_time(stop) / args.steps
-    per_step = step_times_ms(marks)
+    # Timed region: exactly args.steps steps with nothing but the two bracketing events; then
+    # as many with per-step events; then a few instrumented ones for the per-kernel times.
+    def record():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    ms, per_step, stats, prof_steps = timed_passes(one_step, args.steps, record, torch.cuda.synchronize,
+                                                   nm.profile_begin, nm.profile_end)
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step (median {per_step.get('median')}); "
+          f"profiled {prof_steps} more", file=sys.stderr, flush=True)
 
     value = flops / (ms * 1e-3) / 1e12
     # The dominant MFMA kernel: the one with the most time in the timed steps.
@@ -422,16 +475,16 @@ def main() -> int:
     wide_dominant = gemm_name.startswith("gemm_wide")
     traffic = traffic_from_profiles(gemm_name, wl.name,
                                     [(i, c) for i, c in enumerate(cfg_of_launch) if bool(c & 1) == wide_dominant])
-    kernels = {k: {"launches": v["launches"] // args.steps, "ms_per_step": v["ms"] / args.steps,
+    kernels = {k: {"launches": v["launches"] // prof_steps, "ms_per_step": v["ms"] / prof_steps,
                    "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None,
                    "gbs": (v["bytes"] / (v["ms"] * 1e-3) / 1e9) if v["bytes"] else None}
                for k, v in stats.items()}
-    print(f"[bench] {ms:.3f} ms/step; per kernel: {json.dumps(kernels)}", file=sys.stderr, flush=True)
+    print(f"[bench] per kernel: {json.dumps(kernels)}", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, args.cpu_budget)
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl)
 
     dtypes = sorted({s.dtype for s in wl.matrices})
     out = {
@@ -449,7 +502,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "+".join(dtypes),
         "data": "synthetic",
-        "matrices_per_s": round(wl.count / (ms * 1e-3), 2),
+        "matrices_per_s": round(wl.count / (per_step["median"] * 1e-3), 2) if per_step else None,
         "pct_of_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
         "algorithmic_flops_per_step": flops,
         "config": {
@@ -470,9 +523,10 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "launches_per_step": gs["launches"] // args.steps,
+            "launches_per_step": gs["launches"] // prof_steps,
             "avg_launch_ms": round(avg_ms, 5),
             "flops_per_launch": flops_per_launch,
+            "timing": f"HIP events around each launch over {prof_steps} profiled steps after the timed ones",
         },
         "kernels": kernels,
         "cpu_baseline": cpu,

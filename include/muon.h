@@ -164,15 +164,19 @@ int muon_owner_assign(const double* cost, int32_t count, int32_t ranks, int64_t 
  * muon_tune_force say: each piece sums at most an eighth of the contraction, which keeps the
  * fp32 rounding of 2^20-long contractions within the 1e-4 bar.
  *
- * muon_tune: runs one step over device copies of the list's params and momenta (the
- *   caller's matrices are not modified).  After each MFMA launch of that step it times the
- *   same launch in `reps` rounds (1 <= reps <= 64), each round running it once under every
- *   configuration that applies to it.  The configuration with the smallest median time is
- *   stored under the launch's signature when its median is at least 1 % below
- *   configuration 0's, else configuration 0.  A set-up call: it allocates the copies with hipMalloc, frees them
- *   before returning and synchronises the stream.  Arguments and errors as muon_step, plus
- *   MUON_EINVAL for reps outside [1, 64] and MUON_EHIP when the copies cannot be
- *   allocated.
+ * muon_tune_scratch_size: device bytes muon_tune needs in `scratch` for the list (its params
+ *   and momenta, each copy 256-byte aligned); 0 for an empty list.  Host only; errors as
+ *   muon_workspace_size.
+ * muon_tune: runs one step over copies of the list's params and momenta, made in the
+ *   caller's `scratch` (scratch_bytes >= muon_tune_scratch_size, 256-byte aligned, device
+ *   memory the caller owns; the caller's matrices are not modified).  After each MFMA launch
+ *   of that step it times the same launch in `reps` rounds (1 <= reps <= 64), each round
+ *   running it once under every configuration that applies to it.  The configuration with
+ *   the smallest median time is stored under the launch's signature when its median is at
+ *   least 1 % below configuration 0's, else configuration 0.  A set-up call: it synchronises
+ *   the stream before returning, after which the scratch is free again.  Arguments and
+ *   errors as muon_step, plus MUON_EINVAL for reps outside [1, 64] or a NULL or misaligned
+ *   scratch, and MUON_ENOSPC when scratch_bytes is too small (nothing enqueued then).
  * muon_tune_force: cfg in {0, 1, 2, 3} forces that configuration for every launch, -1
  *   restores the table.  MUON_EINVAL for other values.  For tests and measurements.
  * muon_tune_clear: empties the table.
@@ -181,8 +185,9 @@ int muon_owner_assign(const double* cost, int32_t count, int32_t ranks, int64_t 
  *   NUL; buf == NULL only queries it.  MUON_ENOSPC when len is too small (buf untouched).
  * muon_tune_import: adds the lines of such a text to the table (existing signatures are
  *   overwritten).  MUON_EINVAL, with nothing added, on a malformed line.  Host only. */
+int muon_tune_scratch_size(const muon_matrix* mats, int32_t count, const muon_hparams* hp, size_t* bytes);
 int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, void* workspace,
-              size_t workspace_bytes, void* hip_stream, int32_t reps);
+              size_t workspace_bytes, void* scratch, size_t scratch_bytes, void* hip_stream, int32_t reps);
 int muon_tune_force(int32_t cfg);
 void muon_tune_clear(void);
 int muon_tune_export(char* buf, size_t len, size_t* needed);
@@ -207,32 +212,6 @@ typedef struct muon_kernel_stat {
 
 int muon_profile_begin(void);
 int muon_profile_end(muon_kernel_stat* out, int32_t max, int32_t* count);
-
-/* Test hooks (host only): the tile orders used by the MFMA kernel.
- * muon_debug_tile_order: tile t of one matrix -> (ti[t], tj[t]); tri != 0 walks the lower
- * triangle of a tm x tm tile grid, else the full tm x tn grid.  Returns the tile count;
- * ti and tj must hold that many ints.
- * muon_debug_xcd_remap: workgroup w -> logical tile out[w] for a grid of `total`. */
-int muon_debug_tile_order(int tri, int tm, int tn, int* ti, int* tj);
-int muon_debug_xcd_remap(int total, int* out);
-/* muon_debug_wide_tile_order: the same for the 256 x 384 configuration over a rows x cols
- * output: tri != 0 walks the 256 x 384 tiles that meet the lower triangle of a rows x rows
- * output (ti: 256-row band, tj: 384-column band).  Returns the tile count. */
-int muon_debug_wide_tile_order(int tri, int rows, int cols, int* ti, int* tj);
-/* muon_debug_split: the tail split of a launch of `tiles` tiles on `units` compute units
- * whose tail tiles have `ksteps` k-steps each.  plan[0..5] receives the mode (0 none,
- * 1 equal pieces, 2 one uneven cut), the pieces per tail tile (mode 1) or the cut's second
- * pieces per unit (mode 2), the workgroups running whole tiles, the tail tiles, the tail
- * workgroups and the partial-sum slots.  When items is not NULL, items[5 j .. 5 j + 4]
- * receives, for tail workgroup j < max_items, its tail tile, piece, piece count and k-step
- * range [k0, k1), or -1 in the first field for a workgroup without a piece.  Returns the
- * number of tail workgroups, or MUON_EINVAL for a NULL plan or negative sizes. */
-int muon_debug_split(int tiles, int units, int ksteps, int* plan, int* items, int max_items);
-/* muon_debug_flat_loads: on != 0 makes every later 256 x 256 MFMA launch (of muon_step and
- * shampoo_step) address its operands with 64-bit pointers, the path it otherwise takes only
- * when an operand of the launch is 2 GB or larger (below that it uses 32-bit buffer
- * offsets); 0 restores the default.  Process-wide.  For tests of that path. */
-int muon_debug_flat_loads(int32_t on);
 
 const char* muon_strerror(int status); /* static string */
 const char* muon_last_error(void);     /* detail of the last failure on this thread */

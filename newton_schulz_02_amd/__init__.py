@@ -96,7 +96,8 @@ _SIGNATURES = {
     "muon_debug_xcd_remap": (c_int, [c_int, POINTER(c_int)]),
     "muon_owner_assign": (c_int, [POINTER(c_double), c_int32, c_int32, c_int64, POINTER(c_int32),
                                   POINTER(c_double), POINTER(c_int32)]),
-    "muon_tune": (c_int, [_MATP, c_int32, _HPP, c_void_p, c_size_t, c_void_p, c_int32]),
+    "muon_tune_scratch_size": (c_int, [_MATP, c_int32, _HPP, POINTER(c_size_t)]),
+    "muon_tune": (c_int, [_MATP, c_int32, _HPP, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p, c_int32]),
     "muon_tune_force": (c_int, [c_int32]),
     "muon_tune_clear": (None, []),
     "muon_tune_export": (c_int, [c_char_p, c_size_t, POINTER(c_size_t)]),
@@ -219,10 +220,16 @@ def step_raw(arr, count: int, hp: muon_hparams, ws_ptr: int, ws_bytes: int, stre
                            stream_ptr))
 
 
-def tune_raw(arr, count: int, hp: muon_hparams, ws_ptr: int, ws_bytes: int, stream_ptr,
-             reps: int = 5) -> None:
+def tune_scratch_size_raw(arr, count: int, hp: muon_hparams) -> int:
+    n = c_size_t(0)
+    _check(lib().muon_tune_scratch_size(arr, int(count), ctypes.byref(hp), ctypes.byref(n)))
+    return int(n.value)
+
+
+def tune_raw(arr, count: int, hp: muon_hparams, ws_ptr: int, ws_bytes: int, scratch_ptr: int,
+             scratch_bytes: int, stream_ptr, reps: int = 5) -> None:
     _check(lib().muon_tune(arr, int(count), ctypes.byref(hp), c_void_p(ws_ptr), int(ws_bytes),
-                           stream_ptr, int(reps)))
+                           c_void_p(scratch_ptr), int(scratch_bytes), stream_ptr, int(reps)))
 
 
 # MFMA kernel configurations: 256 x 256 and 256 x 384 tiles, each also with the tail split.
@@ -318,14 +325,36 @@ class MuonStep:
 
     def tune(self, stream=None, reps: int = 5) -> None:
         """Time every MFMA launch of this step under each kernel configuration and cache the
-        fastest (``muon_tune``); runs on copies, so params and momenta are unchanged."""
+        fastest (``muon_tune``).  It runs on copies of the params and momenta in a scratch
+        tensor allocated here, so they are unchanged; the call synchronises the stream."""
+        import torch
+
+        need = tune_scratch_size_raw(self.arr, self.count, self.hp)
+        if need == 0:
+            return
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        with torch.cuda.stream(s):
+            scratch = torch.empty(need, dtype=torch.uint8, device=self.device)
         tune_raw(self.arr, self.count, self.hp, self.workspace.data_ptr(), self.workspace.numel(),
-                 _stream_handle(stream, self.device), reps)
+                 scratch.data_ptr(), scratch.numel(), _stream_handle(s, self.device), reps)
 
 
 def muon_step(params, grads, moms, *, stream=None, **hp) -> None:
-    """One Muon step over lists of device tensors (param and momentum updated in place)."""
-    MuonStep(params, grads, moms, **hp)(stream)
+    """One Muon step over lists of device tensors (param and momentum updated in place).
+
+    The throwaway workspace is allocated on the stream the step runs on, so the caching
+    allocator does not hand its block to other work before that stream has finished with it.
+    """
+    import torch
+
+    params = list(params)
+    if not params:
+        return
+    dev = params[0].device
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.stream(s):
+        step = MuonStep(params, grads, moms, **hp)
+    step(s)
 
 
 def adamw_step(p, g, m, v, *, lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
@@ -499,5 +528,15 @@ class ShampooStep:
 
 
 def shampoo_step(params, grads, lefts, rights, *, stream=None, **hp) -> None:
-    """One Shampoo step over lists of fp32 device tensors."""
-    ShampooStep(params, grads, lefts, rights, **hp)(stream)
+    """One Shampoo step over lists of fp32 device tensors.  As muon_step, the throwaway
+    workspace is allocated on the stream the step runs on."""
+    import torch
+
+    params = list(params)
+    if not params:
+        return
+    dev = params[0].device
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.stream(s):
+        step = ShampooStep(params, grads, lefts, rights, **hp)
+    step(s)

@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "../../include/muon.h"
+#include "../../include/muon_test_hooks.h"
 #include "muon_internal.h"
 #include "planner.h"
 #include "shampoo_plan.h"
@@ -350,8 +351,34 @@ int muon_step(const muon_matrix* mats, int32_t count, const muon_hparams* hp, vo
   }
 }
 
+namespace {
+// Bytes of the tuning copies of a list: its params and momenta, each 256-byte aligned.
+size_t tune_scratch_bytes(const muon_matrix* mats, int32_t count) {
+  size_t total = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const size_t bytes = size_t(mats[i].rows) * size_t(mats[i].cols) * (mats[i].dtype == MUON_BF16 ? 2 : 4);
+    total += 2 * ((bytes + 255) / 256 * 256);
+  }
+  return total;
+}
+}  // namespace
+
+int muon_tune_scratch_size(const muon_matrix* mats, int32_t count, const muon_hparams* hp, size_t* bytes) {
+  try {
+    if (!bytes) return fail(MUON_EINVAL, "bytes is NULL");
+    Plan check;
+    std::string err;
+    const int rc = build_plan(mats, count, hp, &check, &err);
+    if (rc != MUON_OK) return fail(rc, err);
+    *bytes = count == 0 ? 0 : tune_scratch_bytes(mats, count);
+    return MUON_OK;
+  } catch (const std::exception& e) {
+    return fail(MUON_EHIP, std::string("exception: ") + e.what());
+  }
+}
+
 int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, void* workspace,
-              size_t workspace_bytes, void* hip_stream, int32_t reps) {
+              size_t workspace_bytes, void* scratch, size_t scratch_bytes, void* hip_stream, int32_t reps) {
   try {
     if (reps < 1 || reps > 64) return fail(MUON_EINVAL, "reps must be in [1, 64]");
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
@@ -364,28 +391,24 @@ int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, vo
       if (count == 0) return MUON_OK;
     }
     // The trial launches re-run in-place phases (momentum, the weight update), so the step
-    // runs on device copies of the params and momenta; the caller's matrices are unchanged.
+    // runs on copies of the params and momenta in the caller's scratch; the caller's
+    // matrices are unchanged.
+    const size_t total = tune_scratch_bytes(mats, count);
+    if (!scratch) return fail(MUON_EINVAL, "scratch is NULL");
+    if (scratch_bytes < total)
+      return fail(MUON_ENOSPC, "tuning scratch too small: " + std::to_string(scratch_bytes) + " < " +
+                                   std::to_string(total) + " bytes");
+    if (reinterpret_cast<uintptr_t>(scratch) % 256 != 0) return fail(MUON_EINVAL, "scratch is not 256-byte aligned");
+    char* copy = static_cast<char*>(scratch);
     std::vector<muon_matrix> shadow(mats, mats + count);
-    std::vector<size_t> off(size_t(count) * 2);
-    size_t total = 0;
-    for (int32_t i = 0; i < count; ++i) {
-      const size_t bytes = size_t(mats[i].rows) * size_t(mats[i].cols) * (mats[i].dtype == MUON_BF16 ? 2 : 4);
-      for (int k = 0; k < 2; ++k) {
-        off[size_t(i) * 2 + k] = total;
-        total += (bytes + 255) / 256 * 256;
-      }
-    }
-    char* copy = nullptr;
-    hipError_t e = hipMalloc(reinterpret_cast<void**>(&copy), total);
-    if (e != hipSuccess) return hip_fail(e, "hipMalloc (tuning copies)");
-    struct Free {
-      char* p;
-      ~Free() { hipFree(p); }
-    } release{copy};
+    hipError_t e = hipSuccess;
+    size_t off = 0;
     for (int32_t i = 0; i < count && e == hipSuccess; ++i) {
       const size_t bytes = size_t(mats[i].rows) * size_t(mats[i].cols) * (mats[i].dtype == MUON_BF16 ? 2 : 4);
-      shadow[size_t(i)].param = copy + off[size_t(i) * 2];
-      shadow[size_t(i)].momentum = copy + off[size_t(i) * 2 + 1];
+      const size_t step = (bytes + 255) / 256 * 256;
+      shadow[size_t(i)].param = copy + off;
+      shadow[size_t(i)].momentum = copy + off + step;
+      off += 2 * step;
       e = hipMemcpyAsync(shadow[size_t(i)].param, mats[i].param, bytes, hipMemcpyDeviceToDevice, s);
       if (e == hipSuccess)
         e = hipMemcpyAsync(shadow[size_t(i)].momentum, mats[i].momentum, bytes, hipMemcpyDeviceToDevice, s);
@@ -452,7 +475,7 @@ int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, vo
       }
     }
     g_prof = prof;
-    const hipError_t es = hipStreamSynchronize(s);  // before the copies are freed
+    const hipError_t es = hipStreamSynchronize(s);  // the caller may reuse the scratch on return
     for (hipEvent_t x : ev)
       if (x) hipEventDestroy(x);
     if (rc != MUON_OK) return rc;

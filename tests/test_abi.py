@@ -338,3 +338,19 @@ def test_product_code_never_reaches_the_oracle():
             text = f.read_text()
             assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
             assert "oracle/" not in text, f
+
+
+def test_product_header_holds_no_test_hooks_and_the_library_allocates_no_device_memory():
+    """muon.h is the product interface: the host-only test hooks live in muon_test_hooks.h.
+    No source of the library calls a device allocator (the caller owns every device buffer;
+    the tuner's copies go to caller scratch)."""
+    root = Path(__file__).resolve().parents[1]
+    product = re.sub(r"/\*.*?\*/", "", (root / "include" / "muon.h").read_text(), flags=re.S)
+    assert "muon_debug_" not in product
+    hooks = (root / "include" / "muon_test_hooks.h").read_text()
+    for name in ("muon_debug_tile_order", "muon_debug_xcd_remap", "muon_debug_split", "muon_debug_flat_loads"):
+        assert name in hooks
+    for src in (root / "newton_schulz_02_amd" / "csrc").glob("*"):
+        text = src.read_text()
+        for call in ("hipMalloc(", "hipMallocAsync(", "hipExtMallocWithFlags(", "hipMallocManaged(", "hipFree("):
+            assert call not in text, f"{src.name} calls {call}"

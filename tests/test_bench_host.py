@@ -61,3 +61,54 @@ def test_step_times_median_and_min():
     st = bench.step_times_ms(marks)
     assert st["median"] == pytest.approx(10.65) and st["min"] == pytest.approx(10.3)
     assert bench.step_times_ms(marks[:1]) == {}
+
+
+class _Clock:
+    """Fake device clock: a step advances it by 10 ms, or by 12 ms while profiling is on."""
+
+    def __init__(self):
+        self.t = 0.0
+        self.profiling = False
+        self.steps = 0
+        self.prof_steps = 0
+
+    def step(self):
+        self.steps += 1
+        self.prof_steps += self.profiling
+        self.t += 12.0 if self.profiling else 10.0
+
+    def record(self):
+        return _Mark(self.t)
+
+
+def test_timed_passes_keep_instrumentation_out_of_the_timed_steps():
+    c = _Clock()
+
+    def begin():
+        c.profiling = True
+
+    def end():
+        c.profiling = False
+        return {"gemm_bf16": {"launches": 3}}
+
+    mean, per_step, stats, n_prof = bench.timed_passes(c.step, 20, c.record, lambda: None, begin, end)
+    assert mean == pytest.approx(10.0)                       # the profiling cost is not in it
+    assert per_step == {"median": pytest.approx(10.0), "min": pytest.approx(10.0)}
+    assert stats == {"gemm_bf16": {"launches": 3}} and n_prof == 5
+    assert c.steps == 20 + 20 + 5 and c.prof_steps == 5      # exactly `steps` steps per timed pass
+    _, _, _, n_small = bench.timed_passes(c.step, 3, c.record, lambda: None, begin, end)
+    assert n_small == 3
+
+
+def test_cpu_baseline_full_and_extrapolated():
+    from newton_schulz_02_amd import workloads as W
+
+    wl = W.custom("bench_host_tiny", [(8, 24), (8, 24), (8, 24), (16, 16)], seed=3)
+    full = bench.cpu_baseline(wl, full=True)
+    part = bench.cpu_baseline(wl, full=False)
+    assert full["extrapolated"] is False and "all 4 matrices" in full["sample"]
+    assert part["extrapolated"] is True and "8x24 x3" in part["sample"] and "16x16 x1" in part["sample"]
+    for r in (full, part):
+        assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
+        assert r["cores"] >= 1 and isinstance(r["blas"], str)
+    assert "layer4096_bf16" in bench.FULL_BASELINE and "many_small_512_bf16" not in bench.FULL_BASELINE

@@ -179,7 +179,25 @@ def test_argument_errors(clean_table):
     hp = nm.make_hparams()
     for reps in (0, 65):
         with pytest.raises(nm.MuonError):
-            nm.tune_raw(nm.shape_array([(64, 64)]), 1, hp, 0, 0, None, reps=reps)
+            nm.tune_raw(nm.shape_array([(64, 64)]), 1, hp, 0, 0, 0, 0, None, reps=reps)
+
+
+def test_tune_scratch_size_and_checks(clean_table):
+    """The copies live in caller scratch: params + momenta, each 256-byte aligned; a short,
+    NULL or misaligned scratch is refused on the host (fake pointers never reach a device)."""
+    hp = nm.make_hparams()
+    shapes = [(64, 64), (100, 30)]
+    arr = nm.shape_array(shapes)
+    need = nm.tune_scratch_size_raw(arr, 2, hp)
+    assert need == 2 * 8192 + 2 * 6144          # 64*64*2 = 8192; 100*30*2 = 6000 -> 6144
+    assert nm.tune_scratch_size_raw(nm.shape_array([]), 0, hp) == 0
+    f32 = nm.shape_array([(10, 10)], dtype=nm.MUON_F32)
+    assert nm.tune_scratch_size_raw(f32, 1, hp) == 2 * 512
+    ws = nm.workspace_size_raw(arr, 2, hp)
+    for ptr, nbytes, status in ((0, need, -1), (1 << 30, need - 1, -2), ((1 << 30) + 16, need, -1)):
+        with pytest.raises(nm.MuonError) as ei:
+            nm.tune_raw(arr, 2, hp, 1 << 36, ws, ptr, nbytes, None, reps=1)
+        assert ei.value.status == status
 
 
 def test_wide_configuration_is_off_for_operands_beyond_32_bit_offsets(clean_table):
