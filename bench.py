@@ -289,6 +289,7 @@ def bench_shampoo(args) -> int:
 
     ms, per_step, stats, prof_steps = timed_passes(lambda: step(stream), args.steps, record,
                                                    torch.cuda.synchronize, nm.profile_begin, nm.profile_end)
+    step.check(stream)
     value = flops / (ms * 1e-3) / 1e12
     gs = stats["gemm_f32"]
     avg_ms = gs["ms"] / gs["launches"]
@@ -461,6 +462,7 @@ def main() -> int:
 
     ms, per_step, stats, prof_steps = timed_passes(one_step, args.steps, record, torch.cuda.synchronize,
                                                    nm.profile_begin, nm.profile_end)
+    step.check(stream)  # the last step's status word (a tail-split timeout would raise here)
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step (median {per_step.get('median')}); "
           f"profiled {prof_steps} more", file=sys.stderr, flush=True)
 

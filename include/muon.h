@@ -150,7 +150,9 @@ int muon_owner_assign(const double* cost, int32_t count, int32_t ranks, int64_t 
  * a launch's last, partial round of workgroups (one per compute unit) are cut along the
  * contraction into pieces run by the otherwise idle units, and the last piece of a tile to
  * finish adds the others' fp32 partial sums in piece order (so results are deterministic,
- * but they may differ from configurations 0 and 1 by the rounding of those additions).  A
+ * but they may differ from configurations 0 and 1 by the rounding of those additions).  The
+ * last piece waits for the others' sums with a bounded wait; should it ever run out, the
+ * tile is stored as NaN and the workspace's status word is set (muon_workspace_check).  A
  * launch with no tail worth cutting runs 2 as 0 and 3 as 1.  Each MFMA launch of a plan has
  * a signature string
  * (dtype, then per shape group its kind, symmetry, orientation and run-length shapes); a
@@ -161,8 +163,12 @@ int muon_owner_assign(const double* cost, int32_t count, int32_t ranks, int64_t 
  * runs configuration 0 (or 2), whatever the table or muon_tune_force say.  An fp32 launch
  * (fp32 matrices, and bf16 ones with at most 128 Gram rows) whose last tiles contract over
  * 2^17 elements or more always runs with the tail split (2 or 3), whatever the table or
- * muon_tune_force say: each piece sums at most an eighth of the contraction, which keeps the
- * fp32 rounding of 2^20-long contractions within the 1e-4 bar.
+ * muon_tune_force say.  Only the launch's tail tiles (those past its last whole round of
+ * one tile per compute unit: all of them when it has fewer tiles than units) are cut: into
+ * 8 pieces when there are at most units/8 of them, into units/R pieces for R tail tiles up
+ * to units/2, and once (about n/(n+1) and 1/(n+1)) beyond that.  Whole-round tiles still
+ * sum the whole contraction in one fp32 sum; they exist only for launches of at least one
+ * tile per unit (an fp32 Gram formation with m above about 5600 rows).
  *
  * muon_tune_scratch_size: device bytes muon_tune needs in `scratch` for the list (its params
  *   and momenta, each copy 256-byte aligned); 0 for an empty list.  Host only; errors as
@@ -212,6 +218,16 @@ typedef struct muon_kernel_stat {
 
 int muon_profile_begin(void);
 int muon_profile_end(muon_kernel_stat* out, int32_t max, int32_t* count);
+
+/* Status of the last step run on a workspace (muon_step or shampoo_step; the first
+ * 256 bytes of every workspace hold a status word that the step's first launch clears).
+ * Synchronises hip_stream, reads the word and clears it.  MUON_OK when the step completed
+ * normally; MUON_EHIP, with the reason in muon_last_error(), when a tail-split tile's bounded
+ * wait for the other pieces' partial sums timed out (that tile was stored as NaN, and the
+ * step's results are not to be used).  MUON_EINVAL for a NULL workspace or
+ * workspace_bytes < 256.  It reports the last step enqueued on the stream before it; check
+ * after every step whose results matter. */
+int muon_workspace_check(void* workspace, size_t workspace_bytes, void* hip_stream);
 
 const char* muon_strerror(int status); /* static string */
 const char* muon_last_error(void);     /* detail of the last failure on this thread */

@@ -40,6 +40,21 @@ int muon_debug_split(int tiles, int units, int ksteps, int* plan, int* items, in
  * when an operand of the launch is 2 GB or larger (below that it uses 32-bit buffer
  * offsets); 0 restores the default.  Process-wide.  For tests of that path. */
 int muon_debug_flat_loads(int32_t on);
+/* muon_debug_split_spins: polls of a tail-split last piece's bounded wait for every later MFMA
+ * launch (spins >= 0); -1 restores the default (about a second); -2 never polls, so every
+ * such wait times out at once: the timeout path runs on the GPU with no wait at all.
+ * Process-wide.  MUON_EINVAL below -2. */
+int muon_debug_split_spins(int32_t spins);
+/* muon_debug_split_protocol: runs the tail split's counter protocol (arrive, publish, collect)
+ * for one tile of `pieces` pieces (2..8) on the host, with the library's own protocol code
+ * over host atomics.  mode 0: each piece on its own thread; 2: the pieces in order; 1: in
+ * order, but piece 0 publishes only after the last piece's wait of `spin_limit` polls ran
+ * out, and then a later launch's pieces arrive on the same counters.  spin_limit -1 never
+ * polls (as the kernels under muon_debug_split_spins(-2)).  out[0..7]: pieces that
+ * took the last-piece role, collect succeeded (1/0), cnt[0] and cnt[1] after, the status
+ * word, slots the last piece saw written (itself included), and for mode 1 cnt[1] after the
+ * late publish and the later launch's pieces that took the last-piece role (else -1). */
+int muon_debug_split_protocol(int32_t pieces, int32_t mode, int32_t spin_limit, int32_t* out);
 
 #ifdef __cplusplus
 }

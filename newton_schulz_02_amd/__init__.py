@@ -105,6 +105,9 @@ _SIGNATURES = {
     "muon_debug_wide_tile_order": (c_int, [c_int, c_int, c_int, POINTER(c_int), POINTER(c_int)]),
     "muon_debug_split": (c_int, [c_int, c_int, c_int, POINTER(c_int), POINTER(c_int), c_int]),
     "muon_debug_flat_loads": (c_int, [c_int32]),
+    "muon_debug_split_spins": (c_int, [c_int32]),
+    "muon_debug_split_protocol": (c_int, [c_int32, c_int32, c_int32, POINTER(c_int32)]),
+    "muon_workspace_check": (c_int, [c_void_p, c_size_t, c_void_p]),
     "shampoo_workspace_size": (c_int, [_SMATP, c_int32, _SHPP, POINTER(c_size_t)]),
     "shampoo_step": (c_int, [_SMATP, c_int32, _SHPP, c_void_p, c_size_t, c_void_p]),
     "shampoo_plan_describe": (c_int, [_SMATP, c_int32, _SHPP, c_char_p, c_size_t]),
@@ -323,6 +326,10 @@ class MuonStep:
         step_raw(self.arr, self.count, self.hp, self.workspace.data_ptr(), self.workspace.numel(),
                  _stream_handle(stream, self.device))
 
+    def check(self, stream=None) -> None:
+        """Raise MuonError if the last step reported a failure (muon_workspace_check)."""
+        workspace_check(self.workspace, stream)
+
     def tune(self, stream=None, reps: int = 5) -> None:
         """Time every MFMA launch of this step under each kernel configuration and cache the
         fastest (``muon_tune``).  It runs on copies of the params and momenta in a scratch
@@ -408,6 +415,25 @@ def flat_loads(on: bool) -> None:
     """Test hook: 64-bit operand pointers in every 256 x 256 launch (the path of operands of
     2 GB and more) instead of 32-bit buffer offsets."""
     _check(lib().muon_debug_flat_loads(1 if on else 0))
+
+
+def split_spins(spins) -> None:
+    """Polls of a tail-split last piece's bounded wait (None: the default)."""
+    _check(lib().muon_debug_split_spins(-1 if spins is None else int(spins)))
+
+
+def split_protocol(pieces: int, mode: int, spin_limit: int) -> list[int]:
+    """Host emulation of the tail split's counter protocol (muon_debug_split_protocol)."""
+    out = (c_int32 * 8)()
+    _check(lib().muon_debug_split_protocol(int(pieces), int(mode), int(spin_limit), out))
+    return list(out)
+
+
+def workspace_check(workspace, stream=None) -> None:
+    """Raise MuonError if the last step on this workspace (a torch uint8 tensor) reported a
+    failure through its status word; synchronises the stream and clears the word."""
+    _check(lib().muon_workspace_check(c_void_p(workspace.data_ptr()), int(workspace.numel()),
+                                      _stream_handle(stream, workspace.device)))
 
 
 def xcd_remap(total: int):
@@ -518,6 +544,10 @@ class ShampooStep:
         if workspace.numel() < self.ws_bytes:
             raise ValueError(f"workspace has {workspace.numel()} bytes, needs {self.ws_bytes}")
         self.workspace = workspace
+
+    def check(self, stream=None) -> None:
+        """Raise MuonError if the last step reported a failure (muon_workspace_check)."""
+        workspace_check(self.workspace, stream)
 
     def plan(self) -> dict:
         return shampoo_plan_describe(self.arr, self.count, self.hp)

@@ -4,7 +4,8 @@
 //               copies that the MFMA phase reads (transpose staged through LDS so both
 //               the read and the write are coalesced);
 //   k_norm      s = 1 / (sqrt(sum of partials) + eps) per matrix, summed in a fixed order
-//               (it also clears the contraction kernels' tail-split counters);
+//               (it also clears the contraction kernels' tail-split counters; the step's
+//               first momentum launch clears them and the workspace's status word too);
 //   k_adamw     AdamW on the packed fp32 tail.
 // Method: DMuon summary §1 (Newton-Schulz on momentum-aggregated gradients); MatrixFSDP
 // summary, Methodology §1 (AdamW for the non-matrix tail).
@@ -79,6 +80,10 @@ __global__ __launch_bounds__(256) void k_momentum(MomArgs a) {
   __shared__ float tile[kEwTile][kEwTile + 1];
   __shared__ float red[4];
 
+  if (a.status && blockIdx.x == 0) {
+    if (threadIdx.x == 0) *a.status = 0;
+    for (int i = threadIdx.x; i < a.split_cnt_n; i += 256) a.split_cnt[i] = 0;
+  }
   const int vt = a.tile_begin + int(blockIdx.x);
   int lo = a.first, hi = a.last - 1;
   while (lo < hi) {

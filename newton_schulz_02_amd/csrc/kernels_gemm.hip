@@ -388,7 +388,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
   // sums to that one; the last adds them in and stores the tile.
   if (pieces > 1 &&
       !split_fixup<4, kFragN>(acc, piece, pieces, cnt, slots, kSlotFloats,
-                              reinterpret_cast<int*>(lds0), idle))
+                              reinterpret_cast<int*>(lds0), idle, args.status,
+                              args.split_spins))
     return;
 
   // ---- epilogue ------------------------------------------------------------------------

@@ -10,6 +10,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "../../include/muon.h"
@@ -17,6 +18,7 @@
 #include "muon_internal.h"
 #include "planner.h"
 #include "shampoo_plan.h"
+#include "split_protocol.h"
 
 using namespace muon;
 
@@ -70,6 +72,8 @@ int g_force_cfg = -1;
 // Test hook: run every 256 x 256 launch with 64-bit operand pointers (the path of operands of
 // 2 GB and more).
 bool g_flat_loads = false;
+// Polls of a tail-split last piece's bounded wait (kSplitSpins; a test hook lowers it).
+int g_split_spins = kSplitSpins;
 
 // Caller holds g_mu.
 int choose_cfg(const std::string& sig) {
@@ -177,10 +181,15 @@ int run_launch(int dev, hipStream_t s, const Plan& plan, const PlanLaunch& L, in
   float* scale = reinterpret_cast<float*>(ws + plan.scale_off);
   float* partials = reinterpret_cast<float*>(ws + plan.partial_off);
   int32_t* split_cnt = reinterpret_cast<int32_t*>(ws + plan.split_cnt_off);
+  int32_t* status = reinterpret_cast<int32_t*>(ws);
   if (L.kind == kLaunchMomentum) {
     MomArgs a;
     a.desc = ddesc;
     a.partials = partials;
+    const bool first = &L == &plan.launches.front();
+    a.status = first ? status : nullptr;
+    a.split_cnt = first ? split_cnt : nullptr;
+    a.split_cnt_n = first ? plan.split_cnt_n : 0;
     a.first = L.first;
     a.last = L.last;
     a.tile_begin = int32_t(plan.mats[L.first].mom_prefix);
@@ -222,6 +231,8 @@ int run_launch(int dev, hipStream_t s, const Plan& plan, const PlanLaunch& L, in
   a.tail_wgs = split ? sp.tail_wgs : 0;
   a.split_cnt = split_cnt;
   a.split_slots = reinterpret_cast<float*>(ws + plan.split_slot_off);
+  a.status = status;
+  a.split_spins = g_split_spins;
   a.grid = a.dp_tiles + a.tail_wgs;
   a.buf32 = (L.buf_ok && !g_flat_loads) ? 1 : 0;
   if (split && (sp.tail > plan.split_cnt_n / 2 || sp.slots > plan.split_slots))
@@ -589,6 +600,95 @@ int shampoo_step(const shampoo_matrix* mats, int32_t count, const shampoo_hparam
   } catch (const std::exception& e) {
     return fail(MUON_EHIP, std::string("exception: ") + e.what());
   }
+}
+
+int muon_workspace_check(void* workspace, size_t workspace_bytes, void* hip_stream) {
+  try {
+    if (!workspace) return fail(MUON_EINVAL, "workspace is NULL");
+    if (workspace_bytes < size_t(kStatusBytes)) return fail(MUON_EINVAL, "workspace smaller than its status word");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    int32_t word = 0;
+    hipError_t e = hipMemcpyAsync(&word, workspace, sizeof word, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "reading the workspace status word");
+    if (word == 0) return MUON_OK;
+    const int32_t zero = 0;
+    e = hipMemcpy(workspace, &zero, sizeof zero, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "clearing the workspace status word");
+    if (word == kStatusSplitTimeout)
+      return fail(MUON_EHIP, "a tail-split wait timed out in the last step on this workspace; "
+                             "the tile it was completing was stored as NaN");
+    return fail(MUON_EHIP, "workspace status word " + std::to_string(word));
+  } catch (const std::exception& e) {
+    return fail(MUON_EHIP, std::string("exception: ") + e.what());
+  }
+}
+
+int muon_debug_split_spins(int32_t spins) {
+  if (spins < -2) return fail(MUON_EINVAL, "muon_debug_split_spins: spins must be >= -2");
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_split_spins = spins == -1 ? kSplitSpins : spins;
+  return MUON_OK;
+}
+
+namespace {
+struct HostSplitOps {
+  int32_t fetch_add(int32_t* p, int32_t v) { return __atomic_fetch_add(p, v, __ATOMIC_SEQ_CST); }
+  int32_t load(int32_t* p) { return __atomic_load_n(p, __ATOMIC_SEQ_CST); }
+  void store(int32_t* p, int32_t v) { __atomic_store_n(p, v, __ATOMIC_SEQ_CST); }
+  void pause() { std::this_thread::yield(); }
+};
+}  // namespace
+
+int muon_debug_split_protocol(int32_t pieces, int32_t mode, int32_t spin_limit, int32_t* out) {
+  if (!out || pieces < 2 || pieces > kMaxPieces || mode < 0 || mode > 2 || spin_limit < -1)
+    return fail(MUON_EINVAL, "muon_debug_split_protocol: bad arguments");
+  int32_t cnt[2] = {0, 0}, status = 0, lasts = 0, ok = -1, seen = 0;
+  int32_t slot[kMaxPieces] = {};
+  HostSplitOps ops;
+  // A piece of the tile: arrive; the others write their slot and publish; the last collects
+  // and then checks that every other slot is written.
+  auto piece = [&](int p, bool publish) {
+    if (split_arrive(ops, cnt, pieces)) {
+      __atomic_fetch_add(&lasts, 1, __ATOMIC_SEQ_CST);
+      const bool good = split_collect(ops, cnt, pieces, spin_limit, &status);
+      __atomic_store_n(&ok, good ? 1 : 0, __ATOMIC_SEQ_CST);
+      if (good) {
+        int n = 0;
+        for (int q = 0; q < pieces; ++q) n += (q == p) || __atomic_load_n(&slot[q], __ATOMIC_SEQ_CST) == q + 1;
+        __atomic_store_n(&seen, n, __ATOMIC_SEQ_CST);
+      }
+    } else if (publish) {
+      __atomic_store_n(&slot[p], p + 1, __ATOMIC_SEQ_CST);
+      split_publish(ops, cnt);
+    }
+  };
+  if (mode == 0) {  // every piece on its own host thread
+    std::vector<std::thread> th;
+    for (int p = 0; p < pieces; ++p) th.emplace_back(piece, p, true);
+    for (std::thread& t : th) t.join();
+  } else {          // in piece order; mode 1: piece 0 arrives but does not publish in time
+    for (int p = 0; p < pieces; ++p) piece(p, !(mode == 1 && p == 0));
+  }
+  out[0] = lasts;
+  out[1] = ok;
+  out[2] = cnt[0];
+  out[3] = cnt[1];
+  out[4] = status;
+  out[5] = seen;
+  out[6] = -1;
+  out[7] = -1;
+  if (mode == 1) {
+    // The stalled piece publishes late; then a later launch's pieces of the same tile
+    // arrive on the uncleared counters: none of them takes the last-piece role.
+    __atomic_store_n(&slot[0], 1, __ATOMIC_SEQ_CST);
+    split_publish(ops, cnt);
+    int32_t later = 0;
+    for (int p = 0; p < pieces; ++p) later += split_arrive(ops, cnt, pieces) ? 1 : 0;
+    out[6] = cnt[1];
+    out[7] = later;
+  }
+  return MUON_OK;
 }
 
 int muon_debug_split(int tiles, int units, int ksteps, int* plan, int* items, int max_items) {

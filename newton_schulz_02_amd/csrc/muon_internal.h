@@ -38,6 +38,7 @@ constexpr int kKPad = 128;       // contraction dimensions are padded to this mu
 constexpr int kEwTile = 64;      // tile edge of the momentum/transpose kernel
 constexpr int kMaxGroups = 8;    // op groups per grouped GEMM launch
 constexpr int kSlots = 5;        // m x m Gram buffers per matrix
+constexpr int64_t kStatusBytes = 256;  // head of every workspace: int32 status word (0 = ok)
 
 enum DType : int32_t { kBF16 = 1, kF32 = 2 };
 
@@ -122,11 +123,18 @@ struct GemmArgs {
   int32_t tail_tiles, tail_wgs;
   int32_t* split_cnt;    // 2 per tail tile: pieces done, partial sums written; 0 between launches
   float* split_slots;    // kSlotFloats per piece of a tail tile
+  int32_t* status;       // the workspace's status word (split_protocol.h)
+  int32_t split_spins;   // polls of a last piece's bounded wait (kSplitSpins)
 };
 
 struct MomArgs {
   const MatDesc* desc;
   float* partials;       // one partial sum of squares per momentum tile
+  // The first launch of a step clears the workspace's status word and the tail-split
+  // counters (workgroup 0, before any contraction of the step runs); null otherwise.
+  int32_t* status;
+  int32_t* split_cnt;
+  int32_t split_cnt_n;
   int32_t first, last;   // matrix range [first, last) of one dtype
   int32_t tile_begin;    // mom_prefix of `first`
   int32_t total_tiles;   // tiles of the range

@@ -365,8 +365,8 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
   plan->levels = max_level + 1;
   plan->total_mom_tiles = mom;
 
-  // Workspace layout.
-  int64_t off = 0;
+  // Workspace layout: the status word, then the descriptors.
+  int64_t off = kStatusBytes;
   plan->desc_off = off;
   off = align_up(off + int64_t(count) * int64_t(sizeof(MatDesc)));
   plan->scale_off = off;

@@ -122,9 +122,10 @@ constexpr int64_t kF32GramMaxM = 128;
 // split whatever the chosen configuration: the MFMA accumulates a tile's products in fp32 in
 // sequence, so its rounding error grows as the square root of the contraction length; at
 // 2^20 (the longest side allowed) that took a 3 x 2^20 fp32 matrix to 1.3e-4 relative error
-// against the 1e-4 bar.  Split pieces keep separate fp32 sums of at most an eighth of the
-// contraction each, added in piece order, and the launch (a Gram formation of at most 136
-// tiles for m <= 4096: all of them tail tiles) spreads over more compute units.
+// against the 1e-4 bar.  Split pieces keep separate fp32 sums, added in piece order: eighths
+// of the contraction when a launch has at most units/8 tail tiles, units/R-ths for R up to
+// units/2, halves or so beyond that (tile_order.h, plan_split).  A launch of fewer tiles than
+// units is all tail; the whole-round tiles of a bigger one are not cut.
 constexpr int64_t kF32SplitMinK = int64_t(1) << 17;
 int gram_dtype(int dtype, int64_t m);
 

@@ -347,7 +347,7 @@ int build_shampoo_plan(const shampoo_matrix* mats, int32_t count, const shampoo_
 
   // Workspace: descriptors, scales, partial sums, then per gradient entry G, G^T and Z, per
   // statistic entry its slots.
-  int64_t off = 0;
+  int64_t off = kStatusBytes;  // the status word comes first
   const int64_t entries = 3 * int64_t(count);
   plan.desc_off = off;
   off = align_up(off + entries * int64_t(sizeof(MatDesc)));

@@ -1,16 +1,13 @@
 // Completion of a tile whose contraction the tail split (tile_order.h) cut into pieces run
 // by different workgroups.  Shared by both MFMA kernels; device code only.
 //
-// Protocol, per tail tile, with two counters that are zero before the launch:
-//   1. a piece that has finished its part of the k loop counts itself in cnt[0];
-//   2. every piece but the last to do so stores its fp32 partial sums in its own slot,
-//      waits until the stores are complete and counts them in cnt[1];
-//   3. the last piece waits until cnt[1] shows the other pieces' sums, adds them to its own
-//      in piece order, clears both counters and goes on to the tile's epilogue.
-// The wait in 3 is for workgroups that have already passed step 1: they are running and
-// need nothing from anyone to finish step 2, so it always ends; it is bounded all the same.
-// Adding in piece order makes the result independent of which piece finishes last: each
-// element is ((p0 + p1) + p2) + ..., the own piece taken from registers at its place.
+// The counter protocol (arrive, publish, collect, and what a timeout leaves behind) is in
+// split_protocol.h, shared with a host emulation.  Here: every piece but the last stores its
+// fp32 partial sums in its own slot before publishing; the last piece adds the others' sums
+// to its own in piece order and goes on to the tile's epilogue, or, if its bounded wait ran
+// out, stores NaN for the whole tile.  Adding in piece order makes the result independent
+// of which piece finishes last: each element is ((p0 + p1) + p2) + ..., the own piece taken
+// from registers at its place.
 //
 // Coherence.  The pieces of a tile may run on different XCDs, whose L2 caches are not
 // coherent with each other.  Every access to a slot and to the counters is made at device
@@ -25,7 +22,19 @@
 
 #include <cstdint>
 
+#include "split_protocol.h"
+
 namespace muon {
+
+// Device-scope atomics of the protocol (the pieces of a tile may run on different XCDs).
+struct DeviceSplitOps {
+  __device__ int32_t fetch_add(int32_t* p, int32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ int32_t load(int32_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+  __device__ void store(int32_t* p, int32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+  __device__ void pause() { __builtin_amdgcn_s_sleep(8); }
+};
 
 // Accumulator layout shared by writer and reader (both run the same kernel and tile shape):
 // float4 number ((wave * FM + i) * FN + j) * 4 + r4 of a slot holds lane-interleaved values
@@ -37,12 +46,15 @@ typedef unsigned int split_u32x4 __attribute__((ext_vector_type(4)));
 
 template <int FM, int FN, typename Acc>
 __device__ __forceinline__ bool split_fixup(Acc (&acc)[FM][FN], int piece, int pieces, int32_t* cnt,
-                                            float* slots, int64_t slot_floats, int* flag, bool idle) {
+                                            float* slots, int64_t slot_floats, int* flag, bool idle,
+                                            int32_t* status, int spin_limit) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) *flag = __hip_atomic_fetch_add(&cnt[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  DeviceSplitOps ops;
+  if (tid == 0) *flag = split_arrive(ops, cnt, pieces) ? 1 : 0;
   __syncthreads();
-  const bool last = *flag == pieces - 1;
+  const bool last = *flag != 0;
+  __syncthreads();  // every thread has read the flag before it is reused below
   // The tile's slots as one buffer (at most kMaxPieces x 384 KB); byte offset of float4 q of
   // slot p: (p slot_floats + 4 q) 4.
   const __amdgpu_buffer_rsrc_t rsrc =
@@ -67,19 +79,20 @@ __device__ __forceinline__ bool split_fixup(Acc (&acc)[FM][FN], int piece, int p
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete (visible to every XCD)
     __syncthreads();
-    if (tid == 0) __hip_atomic_fetch_add(&cnt[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) split_publish(ops, cnt);
     return false;
   }
-  if (tid == 0) {
-    // Bounded wait (a few seconds); see the file comment.
-    for (int spins = 0; spins < (1 << 22); ++spins) {
-      if (__hip_atomic_load(&cnt[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= pieces - 1) break;
-      __builtin_amdgcn_s_sleep(8);
-    }
-    __hip_atomic_store(&cnt[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&cnt[1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (tid == 0) *flag = split_collect(ops, cnt, pieces, spin_limit, status) ? 1 : 0;
   __syncthreads();  // the slot loads below are issued after the count was seen
+  if (*flag == 0) {  // timed out: the tile is stored as NaN, and the status word says why
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_nanf("");
+    return true;
+  }
   auto load = [&](int p, int i, int j, int r4) -> float4 {
     return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, at(p, i, j, r4), 0, kCpolDevice));
   };

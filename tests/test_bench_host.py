@@ -21,8 +21,10 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
 
 
-def test_traffic_follows_the_summary_while_the_hash_matches():
+def test_traffic_follows_the_summary_while_the_hash_matches(monkeypatch):
     text = (ROOT / "profiles" / "gemm_layer4096_bf16_hbm_traffic.md").read_text()
+    recorded = text.split("kernel_hash gemm_bf16:")[1].split()[0]
+    monkeypatch.setattr(bench, "kernel_hash", lambda kernel="gemm_bf16": recorded)
     rows = {c: [float(x) for x in text.split(f"launch_bytes cfg{c}:")[1].splitlines()[0].split(",")]
             for c in range(4)}
     assert all(len(v) == 16 for v in rows.values())
@@ -40,8 +42,10 @@ def test_traffic_is_withheld_when_the_kernel_changed(monkeypatch):
     assert bench.shampoo_traffic_from_profile("shampoo_layer4096_f32") is None
 
 
-def test_shampoo_traffic_is_the_mean_per_launch():
+def test_shampoo_traffic_is_the_mean_per_launch(monkeypatch):
     text = (ROOT / "profiles" / "gemm_shampoo_layer4096_f32_hbm_traffic.md").read_text()
+    recorded = text.split("kernel_hash gemm_f32:")[1].split()[0]
+    monkeypatch.setattr(bench, "kernel_hash", lambda kernel="gemm_f32": recorded)
     line = [l for l in text.splitlines() if l.startswith("launch_bytes:")][0]
     vals = [float(x) for x in line.split(":", 1)[1].split(",")]
     assert bench.shampoo_traffic_from_profile("shampoo_layer4096_f32") == pytest.approx(

@@ -235,8 +235,8 @@ def test_workspace_regions_are_disjoint(shapes, dtype):
     assert regions[0][0] >= 0 and regions[-1][1] <= d["workspace"]
     for (a0, a1), (b0, b1) in zip(regions, regions[1:]):
         assert a1 <= b0, ((a0, a1), (b0, b1))
-    # Descriptors hold count MatDesc entries before the scales.
-    assert d["desc_off"] == 0 and d["scale_off"] > 0
+    # The status word's 256 bytes come first, then count MatDesc entries before the scales.
+    assert d["desc_off"] == 256 and d["scale_off"] > d["desc_off"]
 
 
 def test_workspace_holds_the_partial_sums():
@@ -287,5 +287,33 @@ def test_long_fp32_contractions_always_split():
         nm.tune_force(nm.CFG_WIDE)
         wide = nm.plan_describe(nm.shape_array([(3, 1 << 20, nm.MUON_F32)]), 1, hp)
         assert wide["launches"][2]["cfg"] == nm.CFG_SQUARE_SPLIT
+    finally:
+        nm.tune_force(None)
+
+
+def test_long_fp32_split_cuts_only_the_tail():
+    """What the long-fp32 rule guarantees, per launch: its tail tiles (all of them below one
+    tile per unit) are cut -- 8 pieces for at most units/8 tail tiles, units/R pieces for R up
+    to units/2, one cut beyond -- and whole-round tiles keep the whole contraction."""
+    hp = nm.make_hparams()
+    k = 1 << 17
+    try:
+        nm.tune_force(nm.CFG_SQUARE)
+        for m, tiles, mode, pieces, dp in ((1024, 10, 1, 8, 0), (4096, 136, 2, 2, 0), (8192, 528, 1, 8, 512)):
+            d = nm.plan_describe(nm.shape_array([(m, k, nm.MUON_F32)]), 1, hp)
+            syrk = d["launches"][2]
+            sp = syrk["split_cfg"][0]
+            assert syrk["tiles"] == tiles and syrk["cfg"] == nm.CFG_SQUARE_SPLIT
+            assert sp["mode"] == mode and sp["dp_tiles"] == dp and sp["tail"] == tiles - dp
+            if mode == 1:
+                assert sp["c"] == pieces
+            # the longest piece of a tail tile, in k-steps of 32 fp32 elements
+            ks = k // 32
+            items = [it for it in nm.split_plan(tiles, 256, ks)[1] if it[0] >= 0]
+            longest = max(k1 - k0 for _, _, _, k0, k1 in items)
+            if mode == 1:
+                assert longest * pieces <= ks + 4 * pieces    # pieces start on 4-k-step units
+            else:
+                assert longest < ks
     finally:
         nm.tune_force(None)
