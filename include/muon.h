@@ -219,12 +219,26 @@ typedef struct muon_kernel_stat {
 int muon_profile_begin(void);
 int muon_profile_end(muon_kernel_stat* out, int32_t max, int32_t* count);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): muon_step with no workspace argument.  The
+ * library holds one 128 MiB scratch array per GPU it runs on (a file-scope device array, for
+ * the life of the process) and runs exactly muon_step's plan and kernels in it, so results
+ * equal muon_step's bitwise.  It calls no device or host allocator: the launch descriptors
+ * reach the device in kernel arguments.  Every call on one GPU shares that GPU's array and
+ * leaves its contents behind (each step clears what must start at zero), so calls that
+ * overlap on one GPU (two streams, two threads) race: serialise them.  A list whose
+ * muon_workspace_size exceeds 128 MiB returns MUON_ENOSPC with nothing enqueued; other
+ * arguments and errors as muon_step.  muon_workspace_check(NULL, 0, stream) reports the
+ * last such step's status on the current device. */
+int muon_step_noalloc(const muon_matrix* mats, int32_t count, const muon_hparams* hp, void* hip_stream);
+
 /* Status of the last step run on a workspace (muon_step or shampoo_step; the first
  * 256 bytes of every workspace hold a status word that the step's first launch clears).
  * Synchronises hip_stream, reads the word and clears it.  MUON_OK when the step completed
  * normally; MUON_EHIP, with the reason in muon_last_error(), when a tail-split tile's bounded
  * wait for the other pieces' partial sums timed out (that tile was stored as NaN, and the
- * step's results are not to be used).  MUON_EINVAL for a NULL workspace or
+ * step's results are not to be used).  A NULL workspace means the current device's
+ * muon_step_noalloc scratch (workspace_bytes is then ignored).  MUON_EINVAL for
  * workspace_bytes < 256.  It reports the last step enqueued on the stream before it; check
  * after every step whose results matter. */
 int muon_workspace_check(void* workspace, size_t workspace_bytes, void* hip_stream);

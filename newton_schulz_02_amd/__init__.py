@@ -108,6 +108,7 @@ _SIGNATURES = {
     "muon_debug_split_spins": (c_int, [c_int32]),
     "muon_debug_split_protocol": (c_int, [c_int32, c_int32, c_int32, POINTER(c_int32)]),
     "muon_workspace_check": (c_int, [c_void_p, c_size_t, c_void_p]),
+    "muon_step_noalloc": (c_int, [_MATP, c_int32, _HPP, c_void_p]),
     "shampoo_workspace_size": (c_int, [_SMATP, c_int32, _SHPP, POINTER(c_size_t)]),
     "shampoo_step": (c_int, [_SMATP, c_int32, _SHPP, c_void_p, c_size_t, c_void_p]),
     "shampoo_plan_describe": (c_int, [_SMATP, c_int32, _SHPP, c_char_p, c_size_t]),
@@ -344,6 +345,28 @@ class MuonStep:
             scratch = torch.empty(need, dtype=torch.uint8, device=self.device)
         tune_raw(self.arr, self.count, self.hp, self.workspace.data_ptr(), self.workspace.numel(),
                  scratch.data_ptr(), scratch.numel(), _stream_handle(s, self.device), reps)
+
+
+def muon_step_noalloc(params, grads, moms, *, stream=None, **hp) -> None:
+    """One Muon step with no workspace argument and no device allocation (the library's
+    per-device scratch array, muon_step_noalloc); calls on one device must not overlap."""
+    import torch
+
+    params = list(params)
+    if not params:
+        return
+    dev = params[0].device
+    arr = matrix_array(params, list(grads), list(moms))
+    h = make_hparams(**hp)
+    _check(lib().muon_step_noalloc(arr, len(params), ctypes.byref(h), _stream_handle(stream, dev)))
+
+
+def noalloc_check(stream=None, device=None) -> None:
+    """Raise MuonError if the last muon_step_noalloc on the current device reported a failure."""
+    import torch
+
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    _check(lib().muon_workspace_check(None, 0, _stream_handle(stream, dev)))
 
 
 def muon_step(params, grads, moms, *, stream=None, **hp) -> None:

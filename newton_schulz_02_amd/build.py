@@ -24,7 +24,7 @@ LIB = PKG / "libmuon.so"
 ARCH = "gfx950"
 
 SOURCES = ["planner.cpp", "shampoo_plan.cpp", "muon_api.cpp", "owner.cpp", "kernels_elementwise.hip", "kernels_gemm.hip",
-           "kernels_gemm_wide.hip"]
+           "kernels_gemm_wide.hip", "noalloc.hip"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

@@ -374,6 +374,45 @@ size_t tune_scratch_bytes(const muon_matrix* mats, int32_t count) {
 }
 }  // namespace
 
+int muon_step_noalloc(const muon_matrix* mats, int32_t count, const muon_hparams* hp, void* hip_stream) {
+  try {
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    std::lock_guard<std::mutex> lock(g_mu);
+    Plan plan;
+    std::string err;
+    const CfgChooser chooser = [](const std::string& sig) { return choose_cfg(sig); };
+    int rc = build_plan(mats, count, hp, &plan, &err, &chooser);
+    if (rc != MUON_OK) return fail(rc, err);
+    if (count == 0) return MUON_OK;
+    int dev = 0;
+    if ((rc = current_device(&dev)) != MUON_OK) return rc;
+    if ((rc = check_device(dev)) != MUON_OK) return rc;
+    if (g_dev[dev].units != plan.units) plan_splits(&plan, g_dev[dev].units);
+    if (plan.ws_bytes > kNoAllocBytes)
+      return fail(MUON_ENOSPC, "muon_step_noalloc: the list needs " + std::to_string(plan.ws_bytes) +
+                                   " bytes of scratch, more than the " + std::to_string(kNoAllocBytes) +
+                                   " it has; use muon_step with a workspace");
+    void* scratch = nullptr;
+    const int e = muon_noalloc_scratch(dev, &scratch);
+    if (e != hipSuccess) return hip_fail(hipError_t(e), "hipGetSymbolAddress (no-allocation scratch)");
+    char* ws = static_cast<char*>(scratch);
+    std::vector<MatDesc> descs;
+    fill_descs(plan, mats, hp, ws, &descs);
+    const int eu = muon_put_words(ws + plan.desc_off, descs.data(), descs.size() * sizeof(MatDesc), s);
+    if (eu != hipSuccess) return hip_fail(hipError_t(eu), "descriptor upload (kernel arguments)");
+    const bool prof = g_prof;
+    g_prof = false;  // no profiling events on this path
+    for (const PlanLaunch& L : plan.launches) {
+      rc = run_launch(dev, s, plan, L, L.cfg, ws, hp, count);
+      if (rc != MUON_OK) break;
+    }
+    g_prof = prof;
+    return rc;
+  } catch (const std::exception& ex) {
+    return fail(MUON_EHIP, std::string("exception: ") + ex.what());
+  }
+}
+
 int muon_tune_scratch_size(const muon_matrix* mats, int32_t count, const muon_hparams* hp, size_t* bytes) {
   try {
     if (!bytes) return fail(MUON_EINVAL, "bytes is NULL");
@@ -604,7 +643,15 @@ int shampoo_step(const shampoo_matrix* mats, int32_t count, const shampoo_hparam
 
 int muon_workspace_check(void* workspace, size_t workspace_bytes, void* hip_stream) {
   try {
-    if (!workspace) return fail(MUON_EINVAL, "workspace is NULL");
+    if (!workspace) {  // the current device's muon_step_noalloc scratch
+      std::lock_guard<std::mutex> lock(g_mu);
+      int dev = 0;
+      const int rc = current_device(&dev);
+      if (rc != MUON_OK) return rc;
+      const int e = muon_noalloc_scratch(dev, &workspace);
+      if (e != hipSuccess) return hip_fail(hipError_t(e), "hipGetSymbolAddress (no-allocation scratch)");
+      workspace_bytes = kNoAllocBytes;
+    }
     if (workspace_bytes < size_t(kStatusBytes)) return fail(MUON_EINVAL, "workspace smaller than its status word");
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     int32_t word = 0;

@@ -39,6 +39,7 @@ constexpr int kEwTile = 64;      // tile edge of the momentum/transpose kernel
 constexpr int kMaxGroups = 8;    // op groups per grouped GEMM launch
 constexpr int kSlots = 5;        // m x m Gram buffers per matrix
 constexpr int64_t kStatusBytes = 256;  // head of every workspace: int32 status word (0 = ok)
+constexpr size_t kNoAllocBytes = size_t(128) << 20;  // scratch of muon_step_noalloc, per device
 
 enum DType : int32_t { kBF16 = 1, kF32 = 2 };
 
@@ -172,3 +173,8 @@ int muon_launch_norm(const muon::NormArgs& a, void* stream);
 int muon_launch_gemm(const muon::GemmArgs& a, int dtype, void* stream);
 int muon_launch_gemm_wide(const muon::GemmArgs& a, int dtype, void* stream);
 int muon_launch_adamw(const muon::AdamArgs& a, void* stream);
+// noalloc.hip: device address of the allocation-free entry point's scratch array on device
+// `dev` (asked of the runtime once per device; that device must be current), and a copy of
+// a small host block (bytes a multiple of 4) to device memory through kernel arguments.
+int muon_noalloc_scratch(int dev, void** ptr);
+int muon_put_words(void* dst, const void* src, size_t bytes, void* stream);
