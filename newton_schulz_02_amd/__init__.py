@@ -124,6 +124,13 @@ def lib() -> ctypes.CDLL:
         if not LIB_PATH.exists():
             raise MuonLibraryMissing(
                 f"{LIB_PATH} not found: build it with `python -m newton_schulz_02_amd.build`")
+        # One HIP runtime per process: PyTorch ships its own libamdhip64, and the library's
+        # dependency must resolve to that one, not to a second copy loaded ahead of it
+        # (device memory and streams come from PyTorch).  So PyTorch loads first.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         handle = ctypes.CDLL(str(LIB_PATH))
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(handle, name)

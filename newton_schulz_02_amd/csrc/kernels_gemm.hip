@@ -89,6 +89,16 @@ static_assert(kInstPerOperand >= 1, "every wave loads part of each operand");
 static_assert(kKPad % (kStages * kRowBytes / 4) == 0 && kKPad % (kStages * kRowBytes / 2) == 0,
               "padded contraction dims must hold whole blocks of stages");
 
+// Element offset, within T-row c of the bf16 epilogue's staged tile, of the chunk holding
+// tile rows r .. r+7 (r a multiple of 8): chunk r / 8 rotated by 2 ((c / 16) mod 4).  With
+// the 528-byte T-row stride, a T-row's chunk q starts at 16-byte bank group (c + q) mod 16.
+// The staging writes (32 consecutive T-rows, one chunk) then meet each group twice, the
+// minimum for 8-byte writes; the store pass's reads (16 lanes: 8 T-rows 8 apart, two
+// adjacent chunks) meet 16 distinct groups.
+__device__ __forceinline__ int tile_chunk(int c, int r) {
+  return (((r >> 3) + 2 * ((c >> 4) & 3)) & (kTile / 8 - 1)) * 8;
+}
+
 // Chunk position of 16-byte chunk c in LDS row r is c ^ swz(r) (a bijection on a row).
 __device__ __forceinline__ int swz(int r) {
   return kRowBytes == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
@@ -412,10 +422,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
   // C (direct) and of C^T (mirror or transposed output) with 16-byte stores.
   if constexpr (sizeof(S) == 2) {
     if (kind != kOpUpdate) {
-      auto t_row = [&](int c) -> uint16_t* {
+      // T-row c holds tile column c, in chunks of 8 rows placed by tile_chunk.
+      auto t_chunk = [&](int c, int r) -> uint16_t* {
         const int q = c / kTRowsPerArr;
         char* base = q == 0 ? lds0 : q == 1 ? lds1 : q == 2 ? lds2 : lds3;
-        return reinterpret_cast<uint16_t*>(base) + (c % kTRowsPerArr) * kTs;
+        return reinterpret_cast<uint16_t*>(base) + (c % kTRowsPerArr) * kTs + tile_chunk(c, r);
       };
       const bool xform = kind == kOpXform;
       // Stage the wave's values; K is the op kind as a compile-time constant.
@@ -423,8 +434,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
         constexpr int K = decltype(kc)::value;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          // The polynomial's iterate: E[gj][gi0 .. gi0+3] = E[gi0 .. gi0+3][gj], 8 bytes per
-          // (j, r4); all 8 loads of this i are issued before any is used.
           u32x2 e4[kFragN][4];
           if constexpr (K == kOpPoly || K == kOpAffine) {
 #pragma unroll
@@ -468,7 +477,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
                 }
                 o[q] = from_f(val, static_cast<uint16_t*>(nullptr));
               }
-              *reinterpret_cast<uint2*>(t_row(lcol) + lrow) = *reinterpret_cast<const uint2*>(o);
+              *reinterpret_cast<uint2*>(t_chunk(lcol, lrow & ~7) + (lrow & 7)) = *reinterpret_cast<const uint2*>(o);
             }
         }
       };
@@ -483,47 +492,63 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
         }
       }
       __syncthreads();
-      // Transposed-side pass: row gj = col0 + c of the output gets tile rows r .. r+7 (an
-      // xform without a transposed output skips it).
-      const bool tpass = !xform || g.c2 >= 0;
+      // Store pass, in 8 x 8 blocks.  Lane l of a wave takes block row 8 sr + (l >> 3) and
+      // block column 8 sc + (l & 7) of one of the wave's two 64 x 64 super-blocks (sr, sc).
+      // Its eight 16-byte LDS reads are the block's columns: runs of 8 elements of rows of
+      // C^T (the mirror, or an xform's transposed output); an 8 x 8 transpose in registers
+      // gives the runs of rows of C (direct).  Eight consecutive lanes cover 128 contiguous
+      // bytes of one output row either way, so each store instruction writes whole lines.
+      // Every output here is a workspace buffer whose stored width (kpad) is a multiple of
+      // kKPad, so a block's 8 columns are stored whole or not at all.  On a symmetric output
+      // a block lies strictly below the diagonal (both sides stored), on it (its lower half
+      // and the mirror of that half, as one symmetric block from the direct side), or
+      // strictly above (nothing stored).
+      const bool tpass = !xform || g.c2 >= 0;  // an xform without a transposed output skips it
       const BufDesc T2 = (xform && g.c2 >= 0) ? d.buf[g.c2] : C;
       const gptr<S> Tp = xform ? to_global(static_cast<S*>(T2.ptr)) : Cp;
       const int64_t ldt = xform ? T2.ld : ldc;
-      const int t_rows = xform ? T2.rows : m;          // valid output rows
-      const int t_cols = xform ? T2.kpad : cstore;     // stored output columns
-      for (int idx = tid; tpass && idx < kTile * 32; idx += kThreads) {
-        const int c = idx / 32, r = (idx % 32) * 8;
-        const int gj = col0 + c, gi = row0 + r;
-        if (gj >= t_rows || gi >= t_cols) continue;
-        if (!xform && gi + 7 <= gj) continue;  // chunk on or above the diagonal
-        Vec8<S> v;
-        *reinterpret_cast<uint4*>(v.v) = *reinterpret_cast<const uint4*>(t_row(c) + r);
-        if (xform || (gi > gj && gi + 7 < t_cols)) {
-          store8(Tp + int64_t(gj) * ldt + gi, v);
-        } else {
-          for (int e = 0; e < 8; ++e)
-            if (gi + e > gj && gi + e < t_cols) Tp[int64_t(gj) * ldt + gi + e] = v.v[e];
-        }
-      }
-      // Direct pass: row gi = row0 + r of C gets tile columns c .. c+7.  Lanes cover 8 rows
-      // by 8 column chunks, so each store instruction writes 8 rows x 128 bytes.
+      const int t_rows = xform ? T2.rows : m;          // valid rows of the transposed side
+      const int t_cols = xform ? T2.kpad : cstore;     // its stored columns
       const int d_rows = xform ? C.rows : m;
       const int d_cols = xform ? C.kpad : cstore;
-      for (int idx = tid; idx < kTile * 32; idx += kThreads) {
-        // 64-lane block b: rows 8 (b % 32) .. +7, chunks 8 (b / 32) .. +7 (columns 64 (b / 32) ..).
-        const int b = idx / 64, l = idx % 64;
-        const int r = 8 * (b % 32) + (l & 7), c = 64 * (b / 32) + 8 * (l >> 3);
-        const int gi = row0 + r, gj = col0 + c;
-        if (gi >= d_rows || gj >= d_cols) continue;
-        if (!xform && gi < gj) continue;      // chunk above the diagonal
-        Vec8<S> v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v.v[e] = t_row(c + e)[r];
-        if (xform || (gi >= gj + 7 && gj + 7 < d_cols)) {
-          store8(Cp + int64_t(gi) * ldc + gj, v);
-        } else {
+      for (int sb = 0; sb < 2; ++sb) {
+        const int sblk = wave + kWaves * sb;  // super-block 0 .. 15
+        const int r = 64 * (sblk >> 2) + 8 * (lane >> 3);
+        const int c = 64 * (sblk & 3) + 8 * (lane & 7);
+        const int gi = row0 + r, gj = col0 + c;
+        if (!xform && gi < gj) continue;
+        const bool diag = !xform && gi == gj;
+        u32x4 blk[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) blk[e] = *reinterpret_cast<const u32x4*>(t_chunk(c + e, r));
+        // Element (r + q, c + e) of the tile is half (q & 1) of dword q / 2 of blk[e].
+        auto elem = [&](int q, int e) -> uint32_t {
+          const uint32_t w = blk[e][q >> 1];
+          return (q & 1) ? (w >> 16) : (w & 0xffffu);
+        };
+        // Transposed side: row gj + e gets tile rows r .. r+7 of column c + e.
+        if (tpass && !diag && gi < t_cols) {
+#pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (gi >= gj + e && gj + e < d_cols) Cp[int64_t(gi) * ldc + gj + e] = v.v[e];
+            if (gj + e < t_rows) store8(Tp + int64_t(gj + e) * ldt + gi, __builtin_bit_cast(Vec8<S>, blk[e]));
+        }
+        // Direct side: row gi + q gets tile columns c .. c+7 of row r + q; on a diagonal
+        // block the elements above the diagonal are the mirrors, (r + e, c + q).
+        if (gj < d_cols) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            if (gi + q >= d_rows) continue;
+            u32x4 o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int e0 = 2 * k, e1 = 2 * k + 1;
+              const uint32_t lo = (diag && e0 > q) ? elem(e0, q) : elem(q, e0);
+              const uint32_t hi = (diag && e1 > q) ? elem(e1, q) : elem(q, e1);
+              o[k] = lo | (hi << 16);
+            }
+            store8(Cp + int64_t(gi + q) * ldc + gj, __builtin_bit_cast(Vec8<S>, o));
+          }
         }
       }
       return;
@@ -545,47 +570,83 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
   constexpr int kRowChunks = kTile / 8;   // chunks per row of a half (32)
   constexpr int kColChunks = 128 / 8;     // chunks per column of a half (16)
   constexpr int kChunksHalf = 128 * kRowChunks;
+  // Accumulators of rows [128 half, 128 half + 128) into the stage arrays.
+  auto stage_half = [&](int half) {
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < kFragN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            ep_at(32 * i + 8 * (r >> 2) + 4 * lk + (r & 3), 64 * wn + 32 * j + lr) = acc[i][j][r];
+    }
+  };
+  if (kind == kOpUpdate) {  // W -= eta * alpha * (A B^T)
+    const float step = d.eta * alpha;
+    // W's element type Wt: S, or bf16 for a bf16 matrix whose Gram iteration ran in fp32.
+    auto update = [&](auto wt) {
+      using Wt = decltype(wt);
+      const gptr<Wt> Wp = to_global(static_cast<Wt*>(C.ptr));
+      constexpr int kPer = kChunksHalf / kThreads;  // chunks per thread and half
+      constexpr int kBatch = sizeof(Wt) == 2 ? kPer : kPer / 2;  // W chunks held at once
+      static_assert(kChunksHalf % kThreads == 0 && kPer % kBatch == 0, "whole chunks per thread");
+      Vec8<Wt> w[kBatch];
+      auto chunk = [&](int u, int& rr, int& cc) {  // chunk u of this thread in a half
+        const int idx = tid + u * kThreads;
+        rr = idx / kRowChunks;
+        cc = (idx % kRowChunks) * 8;
+      };
+      auto load_batch = [&](int half, int b) {
+#pragma unroll
+        for (int v = 0; v < kBatch; ++v) {
+          int rr, cc;
+          chunk(b + v, rr, cc);
+          const int gi = row0 + half * 128 + rr, gj = col0 + cc;
+          if (gi < rows_out && d.wvec && gj + 7 < cols_out) load8<Wt>(Wp + int64_t(gi) * ldc + gj, w[v]);
+        }
+      };
+      for (int half = 0; half < 2; ++half) {
+        // The half's first W chunks are requested before its accumulators are staged, so
+        // their latency overlaps the staging; each batch is one load round trip.
+        load_batch(half, 0);
+        stage_half(half);
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < kPer; b += kBatch) {
+          if (b > 0) load_batch(half, b);
+#pragma unroll
+          for (int v = 0; v < kBatch; ++v) {
+            int rr, cc;
+            chunk(b + v, rr, cc);
+            const int gi = row0 + half * 128 + rr, gj = col0 + cc;
+            if (gi >= rows_out || gj >= cols_out) continue;
+            const gptr<Wt> p = Wp + int64_t(gi) * ldc + gj;
+            if (d.wvec && gj + 7 < cols_out) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                w[v].v[e] = from_f(fmaf(-step, ep_at(rr, cc + e), to_f(w[v].v[e])), static_cast<Wt*>(nullptr));
+              store8(p, w[v]);
+            } else {
+              for (int e = 0; e < 8 && gj + e < cols_out; ++e)
+                p[e] = from_f(fmaf(-step, ep_at(rr, cc + e), to_f(p[e])), static_cast<Wt*>(nullptr));
+            }
+          }
+        }
+        __syncthreads();
+      }
+    };
+    if (sizeof(S) == 4 && d.gram_f32) update(uint16_t());
+    else update(S());
+    return;
+  }
   for (int half = 0; half < 2; ++half) {
     const int hr0 = row0 + half * 128;  // first row of this half
     if (!ident) {
-      if (wm == half) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < kFragN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              ep_at(32 * i + 8 * (r >> 2) + 4 * lk + (r & 3), 64 * wn + 32 * j + lr) = acc[i][j][r];
-      }
+      stage_half(half);
       __syncthreads();
     }
-    if (kind == kOpUpdate) {  // W -= eta * alpha * (A B^T)
-      const float step = d.eta * alpha;
-      // W's element type Wt: S, or bf16 for a bf16 matrix whose Gram iteration ran in fp32.
-      auto update = [&](auto wt) {
-        using Wt = decltype(wt);
-        const gptr<Wt> Wp = to_global(static_cast<Wt*>(C.ptr));
-        for (int idx = tid; idx < kChunksHalf; idx += kThreads) {
-          const int rr = idx / kRowChunks, cc = (idx % kRowChunks) * 8;
-          const int gi = hr0 + rr, gj = col0 + cc;
-          if (gi >= rows_out || gj >= cols_out) continue;
-          const gptr<Wt> p = Wp + int64_t(gi) * ldc + gj;
-          if (d.wvec && gj + 7 < cols_out) {
-            Vec8<Wt> w;
-            load8<Wt>(p, w);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              w.v[e] = from_f(fmaf(-step, ep_at(rr, cc + e), to_f(w.v[e])), static_cast<Wt*>(nullptr));
-            store8(p, w);
-          } else {
-            for (int e = 0; e < 8 && gj + e < cols_out; ++e)
-              p[e] = from_f(fmaf(-step, ep_at(rr, cc + e), to_f(p[e])), static_cast<Wt*>(nullptr));
-          }
-        }
-      };
-      if (sizeof(S) == 4 && d.gram_f32) update(uint16_t());
-      else update(S());
-    } else if (g.tri) {
+    if (g.tri) {
       for (int idx = tid; idx < kChunksHalf; idx += kThreads) {
         const int rr = idx / kRowChunks, cc = (idx % kRowChunks) * 8;
         const int gi = hr0 + rr, gj = col0 + cc;
