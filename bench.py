@@ -433,16 +433,10 @@ def main() -> int:
     t0 = time.perf_counter()
     nm.tune_force({"tuned": None, "square": nm.CFG_SQUARE, "wide": nm.CFG_WIDE,
                    "square-split": nm.CFG_SQUARE_SPLIT, "wide-split": nm.CFG_WIDE_SPLIT}[args.kernel])
-    cache = Path(args.tune_cache) if args.tune_cache else None
+    # A saved table (--tune-cache FILE, versioned by the kernels' source hash) that covers
+    # every launch is reused as it is; otherwise the launches are timed and the file updated.
     if args.kernel == "tuned":
-        if cache and cache.exists():
-            nm.tune_import(cache.read_text())
-        table = nm.tune_table()
-        plan = nm.plan_describe(step.arr, step.count, step.hp)
-        if any(L["signature"] not in table for L in plan["launches"] if L["kind"] == "gemm"):
-            step.tune(stream, reps=args.tune_reps)
-        if cache:
-            cache.write_text(nm.tune_export())
+        step.tune(stream, reps=args.tune_reps, cache=Path(args.tune_cache) if args.tune_cache else False)
     plan = nm.plan_describe(step.arr, step.count, step.hp)
     cfg_of_launch = [L["cfg"] for L in plan["launches"] if L["kind"] == "gemm"]
     print(f"[bench] kernel per MFMA launch ({args.kernel}, {time.perf_counter() - t0:.1f} s): "

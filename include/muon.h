@@ -54,7 +54,8 @@ typedef enum muon_status {
   MUON_EALIAS = -3,      /* grad overlaps an output (param/momentum) of any matrix, or
                             outputs of two matrices overlap */
   MUON_EHIP = -4,        /* a HIP runtime call failed; muon_last_error() has the text */
-  MUON_EUNSUPPORTED = -5 /* valid request this library cannot run (e.g. no gfx950 device) */
+  MUON_EUNSUPPORTED = -5, /* valid request this library cannot run (e.g. no gfx950 device) */
+  MUON_ESTALE = -6        /* a tuning table measured on other kernels (another build) */
 } muon_status;
 
 typedef enum muon_dtype { MUON_BF16 = 1, MUON_F32 = 2 } muon_dtype;
@@ -186,11 +187,18 @@ int muon_owner_assign(const double* cost, int32_t count, int32_t ranks, int64_t 
  * muon_tune_force: cfg in {0, 1, 2, 3} forces that configuration for every launch, -1
  *   restores the table.  MUON_EINVAL for other values.  For tests and measurements.
  * muon_tune_clear: empties the table.
- * muon_tune_export: writes the table as text, one "signature cfg" line per entry, sorted,
- *   NUL-terminated, into buf (len bytes).  *needed (may be NULL) receives the size with the
- *   NUL; buf == NULL only queries it.  MUON_ENOSPC when len is too small (buf untouched).
+ * muon_tune_export: writes the table as text, NUL-terminated, into buf (len bytes): a first
+ *   line "# muon-tune <hash>" naming the kernels it was measured on (muon_kernel_hash),
+ *   then one "signature cfg" line per entry, sorted.  *needed (may be NULL) receives the
+ *   size with the NUL; buf == NULL only queries it.  MUON_ENOSPC when len is too small (buf
+ *   untouched).
  * muon_tune_import: adds the lines of such a text to the table (existing signatures are
- *   overwritten).  MUON_EINVAL, with nothing added, on a malformed line.  Host only. */
+ *   overwritten).  A "# muon-tune <hash>" line naming other kernels than this library's
+ *   makes it MUON_ESTALE, with nothing added (a table is valid only for the kernels it was
+ *   measured on); a text without one is taken as it is; other lines starting with '#' are
+ *   comments.  MUON_EINVAL, with nothing added, on a malformed line.  Host only.
+ * muon_kernel_hash: 16 hex digits identifying the kernel sources this library was built
+ *   from (the version of its tuning tables).  Host only. */
 int muon_tune_scratch_size(const muon_matrix* mats, int32_t count, const muon_hparams* hp, size_t* bytes);
 int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, void* workspace,
               size_t workspace_bytes, void* scratch, size_t scratch_bytes, void* hip_stream, int32_t reps);
@@ -198,6 +206,7 @@ int muon_tune_force(int32_t cfg);
 void muon_tune_clear(void);
 int muon_tune_export(char* buf, size_t len, size_t* needed);
 int muon_tune_import(const char* text);
+const char* muon_kernel_hash(void);
 
 /* Host-side description of the launch plan (buckets, restart sets, launches) as a
  * NUL-terminated JSON string written to buf (truncated to len).  Host only.  For tests. */

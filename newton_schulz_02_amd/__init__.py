@@ -26,6 +26,7 @@ MUON_ENOSPC = -2
 MUON_EALIAS = -3
 MUON_EHIP = -4
 MUON_EUNSUPPORTED = -5
+MUON_ESTALE = -6
 MUON_BF16 = 1
 MUON_F32 = 2
 RESTART_AUTO = 0xFFFFFFFF
@@ -101,6 +102,7 @@ _SIGNATURES = {
     "muon_tune_force": (c_int, [c_int32]),
     "muon_tune_clear": (None, []),
     "muon_tune_export": (c_int, [c_char_p, c_size_t, POINTER(c_size_t)]),
+    "muon_kernel_hash": (c_char_p, []),
     "muon_tune_import": (c_int, [c_char_p]),
     "muon_debug_wide_tile_order": (c_int, [c_int, c_int, c_int, POINTER(c_int), POINTER(c_int)]),
     "muon_debug_split": (c_int, [c_int, c_int, c_int, POINTER(c_int), POINTER(c_int), c_int]),
@@ -271,7 +273,73 @@ def tune_import(text: str) -> None:
 
 
 def tune_table() -> dict:
-    return {sig: int(c) for sig, c in (ln.rsplit(" ", 1) for ln in tune_export().splitlines() if ln)}
+    return {sig: int(c) for sig, c in (ln.rsplit(" ", 1) for ln in tune_export().splitlines()
+                                        if ln and not ln.startswith("#"))}
+
+
+def kernel_hash() -> str:
+    """Hash of the kernel sources the library was built from: the version of its tuning tables."""
+    return lib().muon_kernel_hash().decode()
+
+
+def tune_cache_path() -> Path:
+    """Where tuning tables persist across processes: $MUON_TUNE_CACHE, else a file named for
+    this build's kernels under ~/.cache/newton_schulz_02_amd (so builds never share one)."""
+    import os
+
+    env = os.environ.get("MUON_TUNE_CACHE")
+    if env:
+        return Path(env)
+    return Path.home() / ".cache" / "newton_schulz_02_amd" / f"tune-{kernel_hash()}.txt"
+
+
+def tune_cache_load(path=None) -> bool:
+    """Add a saved tuning table to the library's table.  False (and nothing added) when there
+    is no such file or it was measured on other kernels."""
+    path = Path(path) if path is not None else tune_cache_path()
+    if not path.is_file():
+        return False
+    status = lib().muon_tune_import(path.read_text().encode())
+    if status == MUON_ESTALE:
+        return False
+    _check(status)
+    return True
+
+
+def tune_cache_save(path=None) -> Path:
+    """Write the library's table (with its kernel hash) to the cache file, atomically."""
+    import os
+
+    path = Path(path) if path is not None else tune_cache_path()
+    path.parent.mkdir(parents=True, exist_ok=True)
+    tmp = path.with_name(path.name + f".{os.getpid()}.tmp")
+    tmp.write_text(tune_export())
+    os.replace(tmp, path)
+    return path
+
+
+def launch_signatures(arr, count: int, hp: muon_hparams) -> list:
+    """Tuning keys (signatures) of a step's MFMA launches."""
+    return [L["signature"] for L in plan_describe(arr, count, hp)["launches"] if L["kind"] == "gemm"]
+
+
+def tune_with_cache(arr, count: int, hp: muon_hparams, run_tuning, cache=True) -> bool:
+    """Pick the kernel configuration of each MFMA launch of a step, reusing saved choices.
+
+    With a cache (True: tune_cache_path(); or a path), a saved table is loaded first; if it
+    (with what the process already holds) covers every launch of the step, nothing is timed.
+    Otherwise run_tuning() times the step and the merged table is saved.  Returns whether it
+    timed anything."""
+    path = None if cache is False or cache is None else (tune_cache_path() if cache is True else Path(cache))
+    if path is not None:
+        tune_cache_load(path)
+    table = tune_table()
+    if all(sig in table for sig in launch_signatures(arr, count, hp)):
+        return False
+    run_tuning()
+    if path is not None:
+        tune_cache_save(path)
+    return True
 
 
 def workspace_size(params, grads, moms, **hp) -> int:
@@ -338,20 +406,27 @@ class MuonStep:
         """Raise MuonError if the last step reported a failure (muon_workspace_check)."""
         workspace_check(self.workspace, stream)
 
-    def tune(self, stream=None, reps: int = 5) -> None:
-        """Time every MFMA launch of this step under each kernel configuration and cache the
+    def tune(self, stream=None, reps: int = 5, cache=False) -> bool:
+        """Time every MFMA launch of this step under each kernel configuration and keep the
         fastest (``muon_tune``).  It runs on copies of the params and momenta in a scratch
-        tensor allocated here, so they are unchanged; the call synchronises the stream."""
+        tensor allocated here, so they are unchanged; the call synchronises the stream.
+
+        cache (True: tune_cache_path(), or a path) reuses and extends a table saved by an
+        earlier process for the same kernels: when it covers this step, nothing is timed.
+        Returns whether anything was timed."""
         import torch
 
-        need = tune_scratch_size_raw(self.arr, self.count, self.hp)
-        if need == 0:
-            return
-        s = stream if stream is not None else torch.cuda.current_stream(self.device)
-        with torch.cuda.stream(s):
-            scratch = torch.empty(need, dtype=torch.uint8, device=self.device)
-        tune_raw(self.arr, self.count, self.hp, self.workspace.data_ptr(), self.workspace.numel(),
-                 scratch.data_ptr(), scratch.numel(), _stream_handle(s, self.device), reps)
+        def run_tuning():
+            need = tune_scratch_size_raw(self.arr, self.count, self.hp)
+            if need == 0:
+                return
+            s = stream if stream is not None else torch.cuda.current_stream(self.device)
+            with torch.cuda.stream(s):
+                scratch = torch.empty(need, dtype=torch.uint8, device=self.device)
+            tune_raw(self.arr, self.count, self.hp, self.workspace.data_ptr(), self.workspace.numel(),
+                     scratch.data_ptr(), scratch.numel(), _stream_handle(s, self.device), reps)
+
+        return tune_with_cache(self.arr, self.count, self.hp, run_tuning, cache)
 
 
 def muon_step_noalloc(params, grads, moms, *, stream=None, **hp) -> None:

@@ -9,6 +9,7 @@ generation is disabled for all device code.
 
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -28,6 +29,18 @@ SOURCES = ["planner.cpp", "shampoo_plan.cpp", "muon_api.cpp", "owner.cpp", "kern
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+def kernel_hash() -> str:
+    """Hash of the device sources (every .hip and .h file under csrc), 16 hex digits.
+
+    Compiled into the library (muon_kernel_hash); a tuning table records the hash of the
+    kernels it was measured on, and a library built from other sources refuses it."""
+    h = hashlib.sha256()
+    for p in sorted(CSRC.glob("*.hip")) + sorted(CSRC.glob("*.h")):
+        h.update(p.name.encode())
+        h.update(p.read_bytes())
+    return h.hexdigest()[:16]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and Path(cand).exists():
@@ -35,8 +48,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
-def _compile(src: Path, obj: Path, verbose: bool) -> None:
-    cmd = [hipcc(), "-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{ROOT / 'include'}", f"-I{CSRC}"]
+def _compile(src: Path, obj: Path, verbose: bool, khash: str) -> None:
+    cmd = [hipcc(), "-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{ROOT / 'include'}", f"-I{CSRC}",
+           f'-DMUON_KERNEL_HASH="{khash}"']
     if src.suffix == ".hip":
         cmd += ["-x", "hip", f"--offload-arch={ARCH}", *DEVICE_FLAGS]
     else:
@@ -57,8 +71,9 @@ def _compile(src: Path, obj: Path, verbose: bool) -> None:
 def build(verbose: bool = False) -> Path:
     BUILD.mkdir(exist_ok=True)
     objs = [BUILD / (Path(s).stem + ".o") for s in SOURCES]
+    khash = kernel_hash()
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        futs = [ex.submit(_compile, CSRC / s, o, verbose) for s, o in zip(SOURCES, objs)]
+        futs = [ex.submit(_compile, CSRC / s, o, verbose, khash) for s, o in zip(SOURCES, objs)]
         for f in futs:
             f.result()
     tmp = LIB.with_suffix(".so.tmp")

@@ -22,6 +22,11 @@
 
 using namespace muon;
 
+// Set by the build to the hash of the kernel sources (build.py: kernel_hash).
+#ifndef MUON_KERNEL_HASH
+#define MUON_KERNEL_HASH "unversioned"
+#endif
+
 namespace {
 
 thread_local std::string t_last_error;
@@ -285,6 +290,7 @@ const char* muon_strerror(int status) {
     case MUON_EALIAS: return "overlapping buffers";
     case MUON_EHIP: return "HIP runtime error";
     case MUON_EUNSUPPORTED: return "unsupported device or request";
+    case MUON_ESTALE: return "tuning table of other kernels";
     default: return "unknown status";
   }
 }
@@ -777,9 +783,11 @@ void muon_tune_clear(void) {
   g_tune.clear();
 }
 
+const char* muon_kernel_hash(void) { return MUON_KERNEL_HASH; }
+
 int muon_tune_export(char* buf, size_t len, size_t* needed) {
   std::lock_guard<std::mutex> lock(g_mu);
-  std::string out;
+  std::string out = std::string("# muon-tune ") + MUON_KERNEL_HASH + "\n";
   for (const auto& kv : g_tune) out += kv.first + " " + std::to_string(kv.second) + "\n";
   if (needed) *needed = out.size() + 1;
   if (!buf) return MUON_OK;
@@ -797,6 +805,14 @@ int muon_tune_import(const char* text) {
     const std::string line(p, eol ? size_t(eol - p) : std::strlen(p));
     p = eol ? eol + 1 : p + line.size();
     if (line.empty()) continue;
+    if (line[0] == '#') {
+      // "# muon-tune <hash>": the kernels the table was measured on
+      static const std::string kTag = "# muon-tune ";
+      if (line.compare(0, kTag.size(), kTag) == 0 && line.substr(kTag.size()) != MUON_KERNEL_HASH)
+        return fail(MUON_ESTALE, "tuning table measured on kernels " + line.substr(kTag.size()) +
+                                     ", this library's are " + MUON_KERNEL_HASH);
+      continue;
+    }
     const size_t sp = line.rfind(' ');
     if (sp == std::string::npos || sp == 0 || sp + 1 >= line.size())
       return fail(MUON_EINVAL, "tuning line without 'signature cfg': " + line);

@@ -146,3 +146,41 @@ def test_imported_table_mixes_configurations():
             check_matrix(res, i, wl)
     finally:
         nm.tune_clear()
+
+
+def test_tuning_table_persists_and_is_reused(tmp_path):
+    """muon_tune's choices saved to a cache file (with the kernels' hash) and loaded again
+    (as a new process would, from an empty table): the step is covered, nothing is timed,
+    every launch keeps its configuration, and the step passes the parity bar."""
+    nm.tune_clear()
+    nm.tune_force(None)
+    cache = tmp_path / "tune.txt"
+    try:
+        wl = _mixed_workload(seed=43)
+        items = list(W.generate(wl))
+        params = [w.to(DEV) for _, w, _, _ in items]
+        grads = [g.to(DEV) for _, _, g, _ in items]
+        moms = [m.to(DEV) for _, _, _, m in items]
+        step = nm.MuonStep(params, grads, moms, lr=wl.lr, beta=wl.beta, coeffs=wl.coeffs,
+                           steps=wl.steps, eps=wl.eps)
+        log("case tuning cache: first tuning")
+        assert step.tune(reps=2, cache=cache) is True
+        assert cache.read_text().splitlines()[0] == f"# muon-tune {nm.kernel_hash()}"
+        table = nm.tune_table()
+        cfgs = [L["cfg"] for L in nm.plan_describe(step.arr, step.count, step.hp)["launches"] if L["kind"] == "gemm"]
+        nm.tune_clear()
+        log("case tuning cache: reload")
+        assert step.tune(reps=2, cache=cache) is False
+        assert nm.tune_table() == table
+        assert [L["cfg"] for L in nm.plan_describe(step.arr, step.count, step.hp)["launches"]
+                if L["kind"] == "gemm"] == cfgs
+        step()
+        torch.cuda.synchronize()
+        res = {"specs": [s for s, _, _, _ in items], "W0": [w for _, w, _, _ in items],
+               "G": [g for _, _, g, _ in items], "M0": [m for _, _, _, m in items],
+               "W1": [p.cpu() for p in params], "M1": [m.cpu() for m in moms]}
+        for i in range(wl.count):
+            check_matrix(res, i, wl)
+    finally:
+        nm.tune_force(None)
+        nm.tune_clear()

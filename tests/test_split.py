@@ -202,7 +202,7 @@ def test_split_choices_import_and_export(clean_table):
     sig = gemms[1]["signature"]
     nm.tune_import(f"{sig} 2\n")
     assert nm.tune_table() == {sig: 2}
-    assert nm.tune_export() == f"{sig} 2\n"
+    assert nm.tune_export() == f"# muon-tune {nm.kernel_hash()}\n{sig} 2\n"
     _, gemms = _gemms(LAYER)
     assert [L["cfg"] for L in gemms if L["signature"] == sig] == [2] * sum(
         L["signature"] == sig for L in gemms)

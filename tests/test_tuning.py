@@ -6,6 +6,8 @@ from __future__ import annotations
 
 import itertools
 
+from pathlib import Path
+
 import pytest
 
 import newton_schulz_02_amd as nm
@@ -150,12 +152,15 @@ def test_table_and_force_select_the_configuration(clean_table):
 
 
 def test_export_import_round_trip(clean_table):
-    assert nm.tune_export() == ""
+    head = f"# muon-tune {nm.kernel_hash()}\n"
+    assert nm.tune_export() == head
     text = "bf16|0:1:0:640x640*1 1\nbf16|4:0:1:100x300*1 0\nf32|2:1:0:64x64*3 1\n"
     nm.tune_import(text)
     out = nm.tune_export()
-    assert sorted(out.splitlines()) == sorted(text.splitlines())
-    assert out == "".join(sorted(ln + "\n" for ln in text.splitlines()))  # sorted by signature
+    assert out.startswith(head)
+    body = out[len(head):]
+    assert sorted(body.splitlines()) == sorted(text.splitlines())
+    assert body == "".join(sorted(ln + "\n" for ln in text.splitlines()))  # sorted by signature
     nm.tune_clear()
     nm.tune_import(out)
     assert nm.tune_export() == out
@@ -212,3 +217,121 @@ def test_wide_configuration_is_off_for_operands_beyond_32_bit_offsets(clean_tabl
             has_big = f"{d}x{d}" in L["signature"]
             assert L["wide_ok"] == (ok or not has_big)
             assert L["cfg"] == (1 if L["wide_ok"] else 0)
+
+
+# ---- persistent tuning tables, versioned by the kernels they were measured on ----------------
+
+def test_the_table_names_the_kernels_it_was_measured_on(clean_table):
+    """The exported table's first line is the hash of the kernel sources the library was
+    built from; that is the hash of the sources in this tree (the library is current)."""
+    from newton_schulz_02_amd.build import kernel_hash
+
+    assert nm.kernel_hash() == kernel_hash()
+    assert len(nm.kernel_hash()) == 16 and int(nm.kernel_hash(), 16) >= 0
+    assert nm.tune_export().splitlines()[0] == f"# muon-tune {nm.kernel_hash()}"
+
+
+def test_a_table_of_other_kernels_is_refused(clean_table):
+    nm.tune_import("keep 1\n")
+    other = "0" * 16 if nm.kernel_hash() != "0" * 16 else "1" * 16
+    with pytest.raises(nm.MuonError) as ei:
+        nm.tune_import(f"# muon-tune {other}\nnew 0\n")
+    assert ei.value.status == nm.MUON_ESTALE
+    assert nm.tune_table() == {"keep": 1}
+    # its own hash, comments and a text without the line are accepted
+    nm.tune_import(f"# muon-tune {nm.kernel_hash()}\n# a comment\nnew 0\n")
+    nm.tune_import("plain 1\n")
+    assert nm.tune_table() == {"keep": 1, "new": 0, "plain": 1}
+
+
+def test_cache_file_round_trip(clean_table, tmp_path, monkeypatch):
+    monkeypatch.setenv("MUON_TUNE_CACHE", str(tmp_path / "tune.txt"))
+    assert nm.tune_cache_path() == tmp_path / "tune.txt"
+    assert not nm.tune_cache_load()  # no file yet
+    nm.tune_import("bf16|0:1:0:640x640*1 1\nf32|2:1:0:64x64*3 0\n")
+    path = nm.tune_cache_save()
+    assert path.read_text() == nm.tune_export()
+    nm.tune_clear()
+    assert nm.tune_cache_load()
+    assert nm.tune_table() == {"bf16|0:1:0:640x640*1": 1, "f32|2:1:0:64x64*3": 0}
+
+
+def test_default_cache_path_is_named_for_the_kernels(monkeypatch):
+    monkeypatch.delenv("MUON_TUNE_CACHE", raising=False)
+    assert nm.tune_cache_path().name == f"tune-{nm.kernel_hash()}.txt"
+
+
+LIST = [(1024, 4096)] * 3 + [(2048, 2048)]
+
+
+def _fake_tuner(calls, cfg=1):
+    """Stands in for muon_tune (which needs a GPU): records the call and enters a choice for
+    every launch of the step, as the tuner does."""
+    def run():
+        calls.append(1)
+        sigs = nm.launch_signatures(nm.shape_array(LIST), len(LIST), nm.make_hparams())
+        nm.tune_import("".join(f"{s} {cfg}\n" for s in dict.fromkeys(sigs)))
+    return run
+
+
+def test_a_saved_table_is_reused_without_timing(clean_table, tmp_path):
+    arr, hp, cache = nm.shape_array(LIST), nm.make_hparams(), tmp_path / "tune.txt"
+    calls = []
+    assert nm.tune_with_cache(arr, len(LIST), hp, _fake_tuner(calls), cache) is True
+    assert calls == [1] and cache.is_file()
+    table = nm.tune_table()
+    # a new process: the table is empty; the saved one covers the step, so nothing is timed
+    nm.tune_clear()
+    assert nm.tune_with_cache(arr, len(LIST), hp, _fake_tuner(calls), cache) is False
+    assert calls == [1]
+    assert nm.tune_table() == table
+    cfgs = [L["cfg"] for L in nm.plan_describe(arr, len(LIST), hp)["launches"] if L["kind"] == "gemm"]
+    assert cfgs and all(c == 1 for c in cfgs)
+
+
+def test_a_stale_or_partial_table_is_timed_again(clean_table, tmp_path):
+    arr, hp, cache = nm.shape_array(LIST), nm.make_hparams(), tmp_path / "tune.txt"
+    other = "0" * 16 if nm.kernel_hash() != "0" * 16 else "1" * 16
+    sigs = nm.launch_signatures(arr, len(LIST), hp)
+    cache.write_text(f"# muon-tune {other}\n" + "".join(f"{s} 3\n" for s in dict.fromkeys(sigs)))
+    calls = []
+    assert nm.tune_with_cache(arr, len(LIST), hp, _fake_tuner(calls), cache) is True
+    assert calls == [1]
+    assert cache.read_text().splitlines()[0] == f"# muon-tune {nm.kernel_hash()}"
+    assert set(nm.tune_table().values()) == {1}
+    # a table that covers only part of the step is completed by timing
+    nm.tune_clear()
+    cache.write_text(f"# muon-tune {nm.kernel_hash()}\n{sigs[0]} 0\n")
+    assert nm.tune_with_cache(arr, len(LIST), hp, _fake_tuner(calls), cache) is True
+    assert calls == [1, 1]
+
+
+def test_no_cache_always_times(clean_table):
+    arr, hp = nm.shape_array(LIST), nm.make_hparams()
+    calls = []
+    nm.tune_with_cache(arr, len(LIST), hp, _fake_tuner(calls), cache=False)
+    assert calls == [1]
+    nm.tune_with_cache(arr, len(LIST), hp, _fake_tuner(calls), cache=False)  # covered already
+    assert calls == [1]
+
+
+def test_a_saved_table_serves_another_process(clean_table, tmp_path):
+    """The cache outlives the process: a second interpreter loads it and finds every launch
+    of the same step chosen, so it would time nothing."""
+    import subprocess
+    import sys
+
+    arr, hp, cache = nm.shape_array(LIST), nm.make_hparams(), tmp_path / "tune.txt"
+    nm.tune_with_cache(arr, len(LIST), hp, _fake_tuner([], cfg=3), cache)
+    code = (
+        "import newton_schulz_02_amd as nm\n"
+        f"LIST = {LIST!r}\n"
+        "arr, hp = nm.shape_array(LIST), nm.make_hparams()\n"
+        "def never():\n"
+        "    raise SystemExit('timed again')\n"
+        f"assert nm.tune_with_cache(arr, len(LIST), hp, never, {str(cache)!r}) is False\n"
+        "print(sorted(set(nm.tune_table().values())))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                         cwd=str(Path(__file__).resolve().parents[1]))
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "[3]"
