@@ -245,9 +245,10 @@ def tune_raw(arr, count: int, hp: muon_hparams, ws_ptr: int, ws_bytes: int, scra
                            c_void_p(scratch_ptr), int(scratch_bytes), stream_ptr, int(reps)))
 
 
-# MFMA kernel configurations: 256 x 256 and 256 x 384 tiles, each also with the tail split.
-CFG_SQUARE, CFG_WIDE, CFG_SQUARE_SPLIT, CFG_WIDE_SPLIT = 0, 1, 2, 3
-CFG_LABELS = {0: "256x256", 1: "256x384", 2: "256x256+split", 3: "256x384+split"}
+# MFMA kernel configurations: 256 x 256 and 256 x 384 tiles, each also with the tail split,
+# and the 256 x 256 kernel with the deeper load pipeline (4 LDS stages of 64-byte rows).
+CFG_SQUARE, CFG_WIDE, CFG_SQUARE_SPLIT, CFG_WIDE_SPLIT, CFG_SQUARE_DEEP = 0, 1, 2, 3, 4
+CFG_LABELS = {0: "256x256", 1: "256x384", 2: "256x256+split", 3: "256x384+split", 4: "256x256 deep"}
 
 
 def tune_force(cfg) -> None:

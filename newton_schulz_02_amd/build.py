@@ -26,6 +26,8 @@ ARCH = "gfx950"
 
 SOURCES = ["planner.cpp", "shampoo_plan.cpp", "muon_api.cpp", "owner.cpp", "kernels_elementwise.hip", "kernels_gemm.hip",
            "kernels_gemm_wide.hip", "noalloc.hip"]
+# Sources compiled a second time with extra defines: (source, object stem, flags).
+VARIANTS = [("kernels_gemm.hip", "kernels_gemm_deep", ["-DMUON_GEMM_DEEP=1"])]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
@@ -48,9 +50,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
-def _compile(src: Path, obj: Path, verbose: bool, khash: str) -> None:
+def _compile(src: Path, obj: Path, verbose: bool, khash: str, extra=()) -> None:
     cmd = [hipcc(), "-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{ROOT / 'include'}", f"-I{CSRC}",
-           f'-DMUON_KERNEL_HASH="{khash}"']
+           f'-DMUON_KERNEL_HASH="{khash}"', *extra]
     if src.suffix == ".hip":
         cmd += ["-x", "hip", f"--offload-arch={ARCH}", *DEVICE_FLAGS]
     else:
@@ -70,10 +72,12 @@ def _compile(src: Path, obj: Path, verbose: bool, khash: str) -> None:
 
 def build(verbose: bool = False) -> Path:
     BUILD.mkdir(exist_ok=True)
-    objs = [BUILD / (Path(s).stem + ".o") for s in SOURCES]
+    jobs = [(CSRC / s, BUILD / (Path(s).stem + ".o"), ()) for s in SOURCES]
+    jobs += [(CSRC / s, BUILD / (stem + ".o"), tuple(flags)) for s, stem, flags in VARIANTS]
+    objs = [o for _, o, _ in jobs]
     khash = kernel_hash()
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        futs = [ex.submit(_compile, CSRC / s, o, verbose, khash) for s, o in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        futs = [ex.submit(_compile, src, o, verbose, khash, extra) for src, o, extra in jobs]
         for f in futs:
             f.result()
     tmp = LIB.with_suffix(".so.tmp")

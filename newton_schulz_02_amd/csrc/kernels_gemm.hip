@@ -43,6 +43,16 @@
 
 using namespace muon;
 
+// The library builds this file twice: the 256 x 256 kernel with 2 stages of 128-byte rows
+// (muon_launch_gemm), and with MUON_GEMM_DEEP 4 stages of 64-byte rows, three k-steps of
+// loads in flight instead of one (muon_launch_gemm_deep, the deep-pipeline configuration).
+#ifdef MUON_GEMM_DEEP
+#define MUON_GEMM_STAGES 4
+#define MUON_GEMM_ROW_BYTES 64
+#define MUON_LAUNCH_GEMM muon_launch_gemm_deep
+#else
+#define MUON_LAUNCH_GEMM muon_launch_gemm
+#endif
 #ifndef MUON_GEMM_STAGES
 #define MUON_GEMM_STAGES 2
 #endif
@@ -759,7 +769,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
 
 }  // namespace
 
-int muon_launch_gemm(const GemmArgs& a, int dtype, void* stream) {
+int MUON_LAUNCH_GEMM(const GemmArgs& a, int dtype, void* stream) {
   if (a.grid <= 0) return hipSuccess;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == kBF16 && a.buf32)
@@ -773,6 +783,7 @@ int muon_launch_gemm(const GemmArgs& a, int dtype, void* stream) {
   return hipGetLastError();
 }
 
+#ifndef MUON_GEMM_DEEP
 // Test hooks for host-side checks of tile_order.h.
 extern "C" int muon_debug_xcd_remap(int total, int* out) {
   for (int w = 0; w < total; ++w) out[w] = xcd_remap(w, total);
@@ -787,3 +798,4 @@ extern "C" int muon_debug_tile_order(int tri, int tm, int tn, int* ti, int* tj) 
   }
   return n;
 }
+#endif  // MUON_GEMM_DEEP

@@ -243,6 +243,9 @@ int run_launch(int dev, hipStream_t s, const Plan& plan, const PlanLaunch& L, in
   if (split && (sp.tail > plan.split_cnt_n / 2 || sp.slots > plan.split_slots))
     return fail(MUON_EINVAL, "internal: tail split exceeds its workspace");
   const bool bf = L.dtype == kBF16;
+  if (cfg_deep(cfg))
+    return timed(dev, s, bf ? "gemm_deep_bf16" : "gemm_deep_f32", L.flops, 0.0,
+                 [&] { return muon_launch_gemm_deep(a, L.dtype, s); });
   if (shape == kCfgWide)
     return timed(dev, s, bf ? "gemm_wide_bf16" : "gemm_wide_f32", L.flops, 0.0,
                  [&] { return muon_launch_gemm_wide(a, L.dtype, s); });
@@ -513,7 +516,7 @@ int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, vo
           if (e == hipSuccess && rc == MUON_OK) e = hipEventRecord(pair[1], s);
         }
       if (e == hipSuccess && rc == MUON_OK) e = hipStreamSynchronize(s);
-      float med[kNumCfg] = {0.0f, 0.0f, 0.0f, 0.0f};
+      float med[kNumCfg] = {};
       for (int cfg = 0; cfg < kNumCfg && e == hipSuccess; ++cfg) {
         if (!valid[cfg]) continue;
         std::vector<float> t(size_t(reps), 0.0f);
@@ -772,7 +775,7 @@ int muon_debug_flat_loads(int32_t on) {
 }
 
 int muon_tune_force(int32_t cfg) {
-  if (cfg < -1 || cfg >= kNumCfg) return fail(MUON_EINVAL, "cfg must be -1, 0, 1, 2 or 3");
+  if (cfg < -1 || cfg >= kNumCfg) return fail(MUON_EINVAL, "cfg must be -1, 0, 1, 2, 3 or 4");
   std::lock_guard<std::mutex> lock(g_mu);
   g_force_cfg = cfg;
   return MUON_OK;

@@ -19,18 +19,21 @@ constexpr int kTile = 256;       // output tile edge of the square-tile MFMA ker
 constexpr int kWideM = 256;      // output tile rows of the wide-tile MFMA kernel
 constexpr int kWideN = 384;      // output tile columns of the wide-tile MFMA kernel
 // MFMA kernel configurations (chosen per launch: tuned, or the square one by default):
-// bit 0 is the tile shape (256 x 256 or 256 x 384), bit 1 the tail split of the launch's
-// last partial round of workgroups (tile_order.h).
+// for 0..3, bit 0 is the tile shape (256 x 256 or 256 x 384) and bit 1 the tail split of the
+// launch's last partial round of workgroups (tile_order.h); 4 is the 256 x 256 kernel with a
+// deeper load pipeline (4 LDS stages of 64-byte rows, three k-steps of loads in flight).
 enum GemmCfg : int32_t {
   kCfgSquare = 0,
   kCfgWide = 1,
   kCfgSquareSplit = 2,
   kCfgWideSplit = 3,
-  kNumCfg = 4
+  kCfgSquareDeep = 4,
+  kNumCfg = 5
 };
 constexpr int kNumShapes = 2;
 inline int cfg_shape(int cfg) { return cfg & 1; }
 inline bool cfg_split(int cfg) { return (cfg & 2) != 0; }
+inline bool cfg_deep(int cfg) { return cfg == kCfgSquareDeep; }
 constexpr int kMaxUnits = 256;   // compute units a split plans for (MI355X: 256)
 constexpr int kSplitUnit = 4;    // split pieces start and end on multiples of 4 k-steps
 constexpr int64_t kSlotFloats = int64_t(kWideM) * kWideN;  // partial sums of one tile piece
@@ -171,6 +174,7 @@ inline int64_t ceil_div(int64_t x, int64_t q) { return (x + q - 1) / q; }
 int muon_launch_momentum(const muon::MomArgs& a, int dtype, void* stream);
 int muon_launch_norm(const muon::NormArgs& a, void* stream);
 int muon_launch_gemm(const muon::GemmArgs& a, int dtype, void* stream);
+int muon_launch_gemm_deep(const muon::GemmArgs& a, int dtype, void* stream);
 int muon_launch_gemm_wide(const muon::GemmArgs& a, int dtype, void* stream);
 int muon_launch_adamw(const muon::AdamArgs& a, void* stream);
 // noalloc.hip: device address of the allocation-free entry point's scratch array on device

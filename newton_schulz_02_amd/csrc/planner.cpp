@@ -564,8 +564,10 @@ void plan_splits(Plan* plan, int units) {
     int cfg = L.cfg;
     if (cfg < 0 || cfg >= kNumCfg) cfg = kCfgSquare;
     if (cfg_shape(cfg) == kCfgWide && !L.wide_ok) cfg &= ~1;
-    // Long fp32 contractions always run split (accuracy: see kF32SplitMinK).
-    if (L.dtype == kF32 && int64_t(L.kmin_cfg[cfg_shape(cfg)]) * 32 >= kF32SplitMinK) cfg |= 2;
+    // Long fp32 contractions always run split (accuracy: see kF32SplitMinK); the deep
+    // pipeline has no split, so such a launch runs the 256 x 256 split instead.
+    if (L.dtype == kF32 && int64_t(L.kmin_cfg[cfg_shape(cfg)]) * 32 >= kF32SplitMinK)
+      cfg = cfg_deep(cfg) ? int(kCfgSquareSplit) : (cfg | 2);
     if (cfg_split(cfg) && L.split_cfg[cfg_shape(cfg)].mode == kSplitNone) cfg &= ~2;
     L.cfg = cfg;
     const int sh = cfg_shape(cfg);

@@ -169,7 +169,7 @@ def test_export_import_round_trip(clean_table):
     assert nm.tune_table()["bf16|0:1:0:640x640*1"] == 0
 
 
-@pytest.mark.parametrize("bad", ["sig", "sig 4", "sig -1", " 1", "a b 1", "sig 1x", "sig ", "sig 12"])
+@pytest.mark.parametrize("bad", ["sig", "sig 5", "sig -1", " 1", "a b 1", "sig 1x", "sig ", "sig 12"])
 def test_malformed_import_adds_nothing(clean_table, bad):
     nm.tune_import("keep 1\n")
     with pytest.raises(nm.MuonError):
@@ -178,7 +178,7 @@ def test_malformed_import_adds_nothing(clean_table, bad):
 
 
 def test_argument_errors(clean_table):
-    for cfg in (-2, 4, 7):
+    for cfg in (-2, 5, 7):
         with pytest.raises(nm.MuonError):
             nm.tune_force(cfg)
     hp = nm.make_hparams()
