@@ -229,6 +229,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
   __shared__ __attribute__((aligned(1024))) char lds1[kArrBytes];
   __shared__ __attribute__((aligned(1024))) char lds2[kStages > 2 ? kArrBytes : 16];
   __shared__ __attribute__((aligned(1024))) char lds3[kStages > 3 ? kArrBytes : 16];
+  __shared__ int split_flags[2];  // the tail split's flags (split_fixup), apart from the stages
   // Stage array s, named statically when s is a compile-time constant.
   auto stage_of = [&](auto sc) -> char* {
     constexpr int s = decltype(sc)::value % kStages;
@@ -408,7 +409,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
   // sums to that one; the last adds them in and stores the tile.
   if (pieces > 1 &&
       !split_fixup<4, kFragN>(acc, piece, pieces, cnt, slots, kSlotFloats,
-                              reinterpret_cast<int*>(lds0), idle, args.status,
+                              split_flags, idle, args.status,
                               args.split_spins))
     return;
 

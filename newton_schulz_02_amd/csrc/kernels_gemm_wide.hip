@@ -192,7 +192,8 @@ constexpr int kSlabRows = 32;
 template <typename T>
 constexpr int slab_ld() { return kSlabRows + 16 / int(sizeof(T)); }  // 16-byte pad per T-row
 constexpr int kSlabBytes = kWaveCols * (kSlabRows + 4) * 4;          // fp32 staging, the larger
-static_assert(kWaves / 2 * kSlabBytes <= kArrBytes, "per-wave slabs fit the stage arrays");
+static_assert(kWaves / 2 * kSlabBytes + 16 <= kArrBytes,
+              "per-wave slabs fit the stage arrays, clear of the split flags at the end of lds0");
 
 template <typename S>
 struct EpArgs {
@@ -334,6 +335,9 @@ __device__ __forceinline__ void gemm_wide_tile(const GemmArgs& args, const int b
                                                float* const slots) {
   __shared__ __attribute__((aligned(1024))) char lds0[kArrBytes];
   __shared__ __attribute__((aligned(1024))) char lds1[kArrBytes];
+  // The tail split's flags (split_fixup): the last 16 bytes of lds0, which the epilogue's
+  // slabs leave alone (the two stages fill the LDS, so they get no array of their own).
+  int* const split_flags = reinterpret_cast<int*>(lds0 + kArrBytes - 16);
   // Stage array s, named statically when s is a compile-time constant.
   auto stage_of = [&](auto sc) __attribute__((always_inline)) -> char* {
     if constexpr (decltype(sc)::value % kStages == 0) return lds0;
@@ -500,7 +504,7 @@ __device__ __forceinline__ void gemm_wide_tile(const GemmArgs& args, const int b
   // sums to that one; the last adds them in and stores the tile.
   if (pieces > 1 &&
       !split_fixup<kFragM, kFragN>(acc, piece, pieces, cnt, slots, kSlotFloats,
-                                   reinterpret_cast<int*>(lds0), idle, args.status,
+                                   split_flags, idle, args.status,
                                    args.split_spins))
     return;
 

@@ -51,10 +51,12 @@ __device__ __forceinline__ bool split_fixup(Acc (&acc)[FM][FN], int piece, int p
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   DeviceSplitOps ops;
-  if (tid == 0) *flag = split_arrive(ops, cnt, pieces) ? 1 : 0;
+  // flag[0]: the count this piece saw on arrival (kept as the count: reading a 0/1 flag here
+  // instead made the compiler spill inside both kernels' main loops); flag[1]: 0 once the
+  // last piece's wait has seen the others' sums, 1 if it timed out.
+  if (tid == 0) flag[0] = split_arrive_count(ops, cnt);
   __syncthreads();
-  const bool last = *flag != 0;
-  __syncthreads();  // every thread has read the flag before it is reused below
+  const bool last = split_is_last(flag[0], pieces);
   // The tile's slots as one buffer (at most kMaxPieces x 384 KB); byte offset of float4 q of
   // slot p: (p slot_floats + 4 q) 4.
   const __amdgpu_buffer_rsrc_t rsrc =
@@ -82,19 +84,16 @@ __device__ __forceinline__ bool split_fixup(Acc (&acc)[FM][FN], int piece, int p
     if (tid == 0) split_publish(ops, cnt);
     return false;
   }
-  if (tid == 0) *flag = split_collect(ops, cnt, pieces, spin_limit, status) ? 1 : 0;
+  if (tid == 0) flag[1] = split_collect(ops, cnt, pieces, spin_limit, status) ? 0 : 1;
   __syncthreads();  // the slot loads below are issued after the count was seen
-  if (*flag == 0) {  // timed out: the tile is stored as NaN, and the status word says why
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_nanf("");
-    return true;
-  }
+  // Timed out: every partial sum read below is taken as NaN (the loads still stay inside the
+  // slots), so the tile is stored as NaN, and the status word says why.
+  const bool ok = flag[1] == 0;
   auto load = [&](int p, int i, int j, int r4) -> float4 {
-    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, at(p, i, j, r4), 0, kCpolDevice));
+    const float4 x =
+        __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, at(p, i, j, r4), 0, kCpolDevice));
+    const float q = __builtin_nanf("");
+    return ok ? x : make_float4(q, q, q, q);
   };
   if (!idle) {
 #pragma unroll

@@ -30,9 +30,16 @@ namespace muon {
 constexpr int32_t kStatusSplitTimeout = 1;  // status word: a tail-split wait timed out
 constexpr int kSplitSpins = 1 << 22;        // polls of the last piece's wait (about a second)
 
+// Step 1 in two halves: the count the arriving piece saw, and whether that makes it the last.
+template <typename Ops>
+MUON_SPLIT_HD int32_t split_arrive_count(Ops& o, int32_t* cnt) {
+  return o.fetch_add(&cnt[0], 1);
+}
+MUON_SPLIT_HD bool split_is_last(int32_t count, int pieces) { return count == pieces - 1; }
+
 template <typename Ops>
 MUON_SPLIT_HD bool split_arrive(Ops& o, int32_t* cnt, int pieces) {
-  return o.fetch_add(&cnt[0], 1) == pieces - 1;
+  return split_is_last(split_arrive_count(o, cnt), pieces);
 }
 
 template <typename Ops>
