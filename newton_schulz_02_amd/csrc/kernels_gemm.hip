@@ -245,15 +245,25 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
   for (int q = 1; q < kMaxGroups; ++q)
     if (q < args.ngroups && args.g[q].tile_begin <= bid) g = args.g[q];
   const MatDesc* desc = args.desc;
-  const int v = bid - g.tile_begin + (g.tri ? desc[g.first].tri_prefix : desc[g.first].full_prefix);
-  int lo = g.first, hi = g.last - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    const int pre = g.tri ? desc[mid].tri_prefix : desc[mid].full_prefix;
-    if (pre <= v) lo = mid; else hi = mid - 1;
+  // The tile's matrix: a division when the group's matrices have equal tile counts, else a
+  // binary search over the tile prefixes (one dependent descriptor read per step).
+  int lo, t;
+  if (g.tpm > 0) {
+    const int u = bid - g.tile_begin;
+    lo = g.first + u / g.tpm;
+    t = u % g.tpm;
+  } else {
+    const int v = bid - g.tile_begin + (g.tri ? desc[g.first].tri_prefix : desc[g.first].full_prefix);
+    int hi = g.last - 1;
+    lo = g.first;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      const int pre = g.tri ? desc[mid].tri_prefix : desc[mid].full_prefix;
+      if (pre <= v) lo = mid; else hi = mid - 1;
+    }
+    t = v - (g.tri ? desc[lo].tri_prefix : desc[lo].full_prefix);
   }
   const MatDesc& d = desc[lo];
-  const int t = v - (g.tri ? d.tri_prefix : d.full_prefix);
 
   const BufDesc C = d.buf[g.c];
   const int kind = g.kind;

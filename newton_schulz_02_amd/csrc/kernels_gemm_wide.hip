@@ -351,16 +351,26 @@ __device__ __forceinline__ void gemm_wide_tile(const GemmArgs& args, const int b
     if (q < args.ngroups && args.g[q].tile_begin <= bid) g = args.g[q];
   const MatDesc* desc = args.desc;
   // Tile prefixes of this group's output shape: symmetric, full m x n or full n x m.
+  // The tile's matrix: a division when the group's matrices have equal tile counts, else a
+  // binary search over the prefixes.
   const int sel = g.tri ? 0 : (g.nm ? 2 : 1);
-  const int v = bid - g.tile_begin + desc[g.first].wide_prefix[sel];
-  int lo = g.first, hi = g.last - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    const int pre = desc[mid].wide_prefix[sel];
-    if (pre <= v) lo = mid; else hi = mid - 1;
+  int lo, t;
+  if (g.tpm > 0) {
+    const int u = bid - g.tile_begin;
+    lo = g.first + u / g.tpm;
+    t = u % g.tpm;
+  } else {
+    const int v = bid - g.tile_begin + desc[g.first].wide_prefix[sel];
+    int hi = g.last - 1;
+    lo = g.first;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      const int pre = desc[mid].wide_prefix[sel];
+      if (pre <= v) lo = mid; else hi = mid - 1;
+    }
+    t = v - desc[lo].wide_prefix[sel];
   }
   const MatDesc& d = desc[lo];
-  const int t = v - d.wide_prefix[sel];
 
   const BufDesc C = d.buf[g.c];
   const int kind = g.kind;

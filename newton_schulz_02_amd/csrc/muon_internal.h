@@ -106,6 +106,8 @@ struct MatDesc {
 struct GroupArg {
   int32_t first, last;   // matrix range [first, last) in the descriptor table
   int32_t tile_begin;    // first launch tile of this group
+  int32_t tpm = 0;       // tiles per matrix when every matrix of the group has as many (the
+                         // kernel then finds a tile's matrix by a division), else 0
   int8_t kind, a, b, c, c2, e, alpha, tri;  // c2 < 0: an xform stores no transposed copy
   int8_t nm;             // full output of n x m elements (the update of a tall matrix)
 };

@@ -308,8 +308,9 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
     if (a.dtype != b.dtype) return a.dtype < b.dtype;
     if (a.restarts != b.restarts) return a.restarts < b.restarts;
     if (a.tall != b.tall) return a.tall < b.tall;
-    if (a.m != b.m) return a.m < b.m;
-    if (a.n != b.n) return a.n < b.n;
+    // Larger shapes first: inside a launch the tiles then run longest contraction first.
+    if (a.m != b.m) return a.m > b.m;
+    if (a.n != b.n) return a.n > b.n;
     return a.orig < b.orig;
   });
 
@@ -493,13 +494,16 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
           }
           for (int sh = 0; sh < kNumShapes; ++sh) {
             a.tile_begin = int32_t(L.tiles_cfg[sh]);
+            int64_t tpm = -1;
             for (int i = g.first; i < g.last; ++i) {
               const PlanMat& p = plan->mats[i];
               const int64_t nt = sh == kCfgSquare ? (g.op.tri ? p.tri_tiles : p.full_tiles)
                                                   : p.wide_tiles[g.op.tri ? 0 : (a.nm ? 2 : 1)];
               tile_runs[sh].push_back({L.tiles_cfg[sh] + nt, op_ksteps(g.op, p)});
               L.tiles_cfg[sh] += nt;
+              tpm = (tpm < 0 || tpm == nt) ? nt : 0;
             }
+            a.tpm = int32_t(std::max<int64_t>(tpm, 0));
             L.groups_cfg[sh].push_back(a);
           }
           for (int i = g.first; i < g.last; ++i) L.flops += op_flops(g.op, plan->mats[i].m, plan->mats[i].n);
@@ -709,7 +713,8 @@ std::string describe_plan(const Plan& plan) {
     for (size_t g = 0; g < L.groups.size(); ++g) {
       const GroupArg& a = L.groups[g];
       os << (g ? "," : "") << "{\"first\":" << a.first << ",\"last\":" << a.last
-         << ",\"kind\":\"" << kKind[int(a.kind)] << "\",\"tiles_begin\":" << a.tile_begin << "}";
+         << ",\"kind\":\"" << kKind[int(a.kind)] << "\",\"tiles_begin\":" << a.tile_begin
+         << ",\"tpm\":" << a.tpm << "}";
     }
     os << "]}";
   }

@@ -409,10 +409,14 @@ int build_shampoo_plan(const shampoo_matrix* mats, int32_t count, const shampoo_
     a.first = L.first;
     a.last = L.last;
     a.tile_begin = int32_t(L.tiles_cfg[0]);
+    int64_t tpm = -1;
     for (int e = L.first; e < L.last; ++e) {
       const PlanMat& p = plan.mats[size_t(e)];
-      L.tiles_cfg[0] += a.tri ? p.tri_tiles : p.full_tiles;
+      const int64_t nt = a.tri ? p.tri_tiles : p.full_tiles;
+      L.tiles_cfg[0] += nt;
+      tpm = (tpm < 0 || tpm == nt) ? nt : 0;
     }
+    a.tpm = int32_t(std::max<int64_t>(tpm, 0));
     L.groups_cfg[0].push_back(a);
   };
   // K-steps of one tile of group a on entry e: the contraction (padded) over 32 fp32 values.

@@ -66,6 +66,7 @@ CASES = [
     ([(16, 16)], 2, nm.RESTART_AUTO),
     ([(16, 16)], 3, nm.RESTART_AUTO),
     ([(1, 9), (9, 1), (1, 1)], 5, nm.RESTART_AUTO),
+    ([(600, 700), (300, 520), (256, 256), (520, 300)], 3, nm.RESTART_AUTO),
 ]
 
 
@@ -100,11 +101,16 @@ def test_launches_cover_every_op_once(shapes, steps, mask):
         tiles = 0
         for g in L["groups"]:
             assert g["tiles_begin"] == tiles
+            counts = []
             for i in range(g["first"], g["last"]):
                 got.append((i, L["level"], g["kind"]))
                 m, n = mats[i]["m"], mats[i]["n"]
                 t = -(-m // 256)
-                tiles += t * (t + 1) // 2 if g["kind"] in ("syrk", "poly", "prod", "ident") \
-                    else t * -(-n // 256)
+                counts.append(t * (t + 1) // 2 if g["kind"] in ("syrk", "poly", "prod", "ident")
+                              else t * -(-n // 256))
+            tiles += sum(counts)
+            # tiles per matrix: set exactly when the group's matrices have equal tile counts
+            # (the kernels then find a tile's matrix by division instead of a search)
+            assert g["tpm"] == (counts[0] if len(set(counts)) == 1 else 0)
         assert tiles == L["tiles"]
     assert sorted(got) == want
