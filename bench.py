@@ -47,6 +47,7 @@ _COMMON = ["newton_schulz_02_amd/csrc/tile_order.h", "newton_schulz_02_amd/csrc/
 KERNEL_SOURCES = {  # sources each MFMA kernel is built from
     "gemm": ["newton_schulz_02_amd/csrc/kernels_gemm.hip"] + _COMMON,
     "gemm_deep": ["newton_schulz_02_amd/csrc/kernels_gemm.hip"] + _COMMON,
+    "gemm_small": ["newton_schulz_02_amd/csrc/kernels_gemm.hip"] + _COMMON,
     "gemm_wide": ["newton_schulz_02_amd/csrc/kernels_gemm_wide.hip"] + _COMMON,
 }
 
@@ -272,7 +273,7 @@ def bench_shampoo(args) -> int:
     # (default); --kernel square turns it off, for comparison.
     nm.tune_force({"tuned": None, "square": nm.CFG_SQUARE, "wide": nm.CFG_SQUARE,
                    "square-split": nm.CFG_SQUARE_SPLIT, "wide-split": nm.CFG_SQUARE_SPLIT,
-                   "square-deep": nm.CFG_SQUARE}[args.kernel])
+                   "square-deep": nm.CFG_SQUARE, "small": nm.CFG_SQUARE}[args.kernel])
     step = nm.ShampooStep(params, grads, lefts, rights, lr=wl.lr, beta2=wl.beta2, eps=wl.eps,
                           root_iters=wl.root_iters)
     plan = step.plan()
@@ -386,10 +387,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=30.0, help="Shampoo oracle sample only")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
-    ap.add_argument("--kernel", choices=["tuned", "square", "wide", "square-split", "wide-split", "square-deep"],
+    ap.add_argument("--kernel", choices=["tuned", "square", "wide", "square-split", "wide-split", "square-deep",
+                                         "small"],
                     default="tuned",
                     help="MFMA kernel configuration per launch: measured at set-up (tuned) or "
-                         "one fixed (256x256 or 256x384 tiles, optionally with the tail split)")
+                         "one fixed (256x256 or 256x384 tiles, optionally with the tail split; "
+                         "256x256 with the deep load pipeline; 128x128 tiles)")
     ap.add_argument("--tune-reps", type=int, default=5)
     ap.add_argument("--tune-cache", default="", metavar="FILE",
                     help="tuning table to load before set-up (if it exists) and save after")
@@ -435,7 +438,7 @@ def main() -> int:
     t0 = time.perf_counter()
     nm.tune_force({"tuned": None, "square": nm.CFG_SQUARE, "wide": nm.CFG_WIDE,
                    "square-split": nm.CFG_SQUARE_SPLIT, "wide-split": nm.CFG_WIDE_SPLIT,
-                   "square-deep": nm.CFG_SQUARE_DEEP}[args.kernel])
+                   "square-deep": nm.CFG_SQUARE_DEEP, "small": nm.CFG_SMALL}[args.kernel])
     # A saved table (--tune-cache FILE, versioned by the kernels' source hash) that covers
     # every launch is reused as it is; otherwise the launches are timed and the file updated.
     if args.kernel == "tuned":

@@ -146,8 +146,11 @@ int muon_owner_assign(const double* cost, int32_t count, int32_t ranks, int64_t 
 
 /* Shape-adaptive kernel selection (DMuon summary §2.4: the tile shape is searched per
  * target and matrix shape, and the best configuration is cached and reused by later steps).
- * The library has four MFMA kernel configurations: 0 = 256 x 256 output tiles, 1 = 256 x 384
- * output tiles (8 waves of 128 x 96), 2 and 3 = the same with the tail split: the tiles of
+ * The library has six MFMA kernel configurations: 0 = 256 x 256 output tiles, 1 = 256 x 384
+ * output tiles (8 waves of 128 x 96), 4 = 256 x 256 tiles with a deeper load pipeline (four
+ * LDS stages of 32 contraction elements, three k-steps of loads in flight), 5 = 128 x 128
+ * output tiles (4 waves of 64 x 64, two workgroups per compute unit: for launches with fewer
+ * tiles than compute units or short contractions), 2 and 3 = 0 and 1 with the tail split: the tiles of
  * a launch's last, partial round of workgroups (one per compute unit) are cut along the
  * contraction into pieces run by the otherwise idle units, and the last piece of a tile to
  * finish adds the others' fp32 partial sums in piece order (so results are deterministic,
@@ -163,7 +166,7 @@ int muon_owner_assign(const double* cost, int32_t count, int32_t ranks, int64_t 
  * larger side d has (d + 384) * (d rounded up to 128) * element size >= 2^31 bytes always
  * runs configuration 0 (or 2), whatever the table or muon_tune_force say.  An fp32 launch
  * (fp32 matrices, and bf16 ones with at most 128 Gram rows) whose last tiles contract over
- * 2^17 elements or more always runs with the tail split (2 or 3), whatever the table or
+ * 2^17 elements or more always runs with the tail split (3 under 1 or 3, else 2), whatever the table or
  * muon_tune_force say.  Only the launch's tail tiles (those past its last whole round of
  * one tile per compute unit: all of them when it has fewer tiles than units) are cut: into
  * 8 pieces when there are at most units/8 of them, into units/R pieces for R tail tiles up
@@ -184,7 +187,7 @@ int muon_owner_assign(const double* cost, int32_t count, int32_t ranks, int64_t 
  *   the stream before returning, after which the scratch is free again.  Arguments and
  *   errors as muon_step, plus MUON_EINVAL for reps outside [1, 64] or a NULL or misaligned
  *   scratch, and MUON_ENOSPC when scratch_bytes is too small (nothing enqueued then).
- * muon_tune_force: cfg in {0, 1, 2, 3} forces that configuration for every launch, -1
+ * muon_tune_force: cfg in 0 .. 5 forces that configuration for every launch, -1
  *   restores the table.  MUON_EINVAL for other values.  For tests and measurements.
  * muon_tune_clear: empties the table.
  * muon_tune_export: writes the table as text, NUL-terminated, into buf (len bytes): a first

@@ -27,7 +27,8 @@ ARCH = "gfx950"
 SOURCES = ["planner.cpp", "shampoo_plan.cpp", "muon_api.cpp", "owner.cpp", "kernels_elementwise.hip", "kernels_gemm.hip",
            "kernels_gemm_wide.hip", "noalloc.hip"]
 # Sources compiled a second time with extra defines: (source, object stem, flags).
-VARIANTS = [("kernels_gemm.hip", "kernels_gemm_deep", ["-DMUON_GEMM_DEEP=1"])]
+VARIANTS = [("kernels_gemm.hip", "kernels_gemm_deep", ["-DMUON_GEMM_DEEP=1"]),
+            ("kernels_gemm.hip", "kernels_gemm_small", ["-DMUON_GEMM_SMALL=1"])]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

@@ -5,7 +5,8 @@
 // polynomial in G0 = X0 X0^T), so B^T = B, and the row form X and the transposed form
 // X^T are both kept in HBM.  One launch serves several op groups (a group = one op on a
 // contiguous run of same-schedule matrices of one shape bucket; DMuon summary §2.2,
-// batching of similar shapes), and every workgroup computes one 256 x 256 output tile.
+// batching of similar shapes), and every workgroup computes one 256 x 256 output tile
+// (128 x 128 in the small-tile build).
 //
 // Symmetric outputs (DMuon summary §2.2, SYRK-type path over the lower triangle) use the
 // lower-triangle tiles only; each computed element (i >= j) is stored at (i, j) and at
@@ -13,7 +14,7 @@
 //
 // Main loop: 8 waves of 64 lanes in a 2 x 4 grid, each wave owning 128 x 64 = 4 x 2 blocks
 // of 32 x 32 MFMA accumulators (v_mfma_f32_32x32x16_bf16, or v_mfma_f32_32x32x2_f32 for
-// fp32; fp32 accumulate).  A stage holds kRowBytes of every operand row (64 bf16 or 32
+// fp32; fp32 accumulate); the small-tile build has 4 waves in a 2 x 2 grid, 64 x 64 each.  A stage holds kRowBytes of every operand row (64 bf16 or 32
 // fp32 with 128-byte rows).  Operands go straight from global memory to LDS
 // (global_load_lds_dwordx4: 16 bytes per lane, 1 KB per wave instruction), so no VGPRs
 // or LDS-write instructions are spent on staging.  LDS rows are unpadded; the 16-byte
@@ -30,8 +31,8 @@
 // Operand rows past the end of an operand are clamped to its last row: they only feed
 // output rows or columns that are never stored, and every load stays in bounds.
 //
-// Epilogue: the accumulators are staged through LDS as fp32, one 128-row half of the tile
-// at a time, so that the epilogue math reads each input once and both the direct store
+// Epilogue: the accumulators are staged through LDS (bf16 outputs once, transposed; fp32
+// ones one half of the tile at a time), so that the epilogue math reads each input once and both the direct store
 // (rows of C) and the mirrored/transposed store (rows of C^T) are coalesced.
 #include <hip/hip_runtime.h>
 
@@ -43,15 +44,24 @@
 
 using namespace muon;
 
-// The library builds this file twice: the 256 x 256 kernel with 2 stages of 128-byte rows
-// (muon_launch_gemm), and with MUON_GEMM_DEEP 4 stages of 64-byte rows, three k-steps of
-// loads in flight instead of one (muon_launch_gemm_deep, the deep-pipeline configuration).
+// The library builds this file three times: the 256 x 256 kernel with 2 stages of 128-byte
+// rows (muon_launch_gemm); with MUON_GEMM_DEEP 4 stages of 64-byte rows, three k-steps of
+// loads in flight instead of one (muon_launch_gemm_deep, the deep-pipeline configuration);
+// and with MUON_GEMM_SMALL 128 x 128 tiles run by 4 waves of 64 x 64, whose 64 KB of LDS
+// let two workgroups share a compute unit, one's epilogue overlapping the other's
+// contraction (muon_launch_gemm_small, for launches with few tiles or short contractions).
 #ifdef MUON_GEMM_DEEP
 #define MUON_GEMM_STAGES 4
 #define MUON_GEMM_ROW_BYTES 64
 #define MUON_LAUNCH_GEMM muon_launch_gemm_deep
+#elif defined(MUON_GEMM_SMALL)
+#define MUON_GEMM_TILE 128
+#define MUON_LAUNCH_GEMM muon_launch_gemm_small
 #else
 #define MUON_LAUNCH_GEMM muon_launch_gemm
+#endif
+#ifndef MUON_GEMM_TILE
+#define MUON_GEMM_TILE 256
 #endif
 #ifndef MUON_GEMM_STAGES
 #define MUON_GEMM_STAGES 2
@@ -68,33 +78,42 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kThreads = 512;
+constexpr int kT = MUON_GEMM_TILE;             // output tile edge (256, or 128)
+constexpr int kThreads = kT == 256 ? 512 : 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kWavesN = 4;                     // waves along the tile columns
-constexpr int kFragN = kTile / kWavesN / 32;   // 32-wide blocks per wave along N (2)
+constexpr int kWavesN = kWaves / 2;            // waves along the tile columns (2 along the rows)
+constexpr int kWaveRows = kT / 2;              // rows of a wave's block (128, or 64)
+constexpr int kWaveCols = kT / kWavesN;        // columns of a wave's block (64)
+constexpr int kFragM = kWaveRows / 32;         // 32-row MFMA blocks per wave (4, or 2)
+constexpr int kFragN = kWaveCols / 32;         // 32-column MFMA blocks per wave (2)
+constexpr int kHalf = kT / 2;                  // rows of one fp32 epilogue half
+constexpr int kSuper = (kT / 64) * (kT / 64);  // 64 x 64 super-blocks of the store pass
 constexpr int kStages = MUON_GEMM_STAGES;
-constexpr int kEpLd = kTile / kStages + 1;     // fp32 leading dimension of a staged block
+constexpr int kEpLd = kT / kStages + 1;        // fp32 leading dimension of a staged block
                                                // (odd: strided reads spread over the banks)
 constexpr int kRowBytes = MUON_GEMM_ROW_BYTES; // bytes of one operand row per stage
 constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks per row
-constexpr int kOperandBytes = kTile * kRowBytes;
+constexpr int kOperandBytes = kT * kRowBytes;
 constexpr int kStageBytes = 2 * kOperandBytes;
 constexpr int kRowsPerInst = 1024 / kRowBytes; // rows one wave instruction fills
 constexpr int kInstPerOperand = kOperandBytes / 1024 / kWaves;  // per wave per stage
-// The epilogue stages a 128-row half tile in fp32, split by column block across the stage
+// The epilogue stages a half tile (kHalf rows) in fp32, split by column block across the stage
 // arrays: array q holds columns [q kEpW, (q + 1) kEpW) with leading dimension kEpLd.
-constexpr int kEpW = kTile / kStages;
-constexpr int kEpArrBytes = 128 * kEpLd * 4;
+constexpr int kEpW = kT / kStages;
+constexpr int kEpArrBytes = kHalf * kEpLd * 4;
 // bf16 outputs of the Gram products and re-anchors are staged once, transposed: T-row c
 // (a tile column) holds the 256 tile rows; the T-rows are split evenly over the arrays.
-constexpr int kTs = kTile + 8;                 // bf16 T-row stride (528 bytes: 16-byte aligned)
-constexpr int kTRowsPerArr = kTile / kStages;
+constexpr int kTs = kT + 8;                 // bf16 T-row stride (528 bytes: 16-byte aligned)
+constexpr int kTRowsPerArr = kT / kStages;
 constexpr int kTArrBytes = kTRowsPerArr * kTs * 2;
 constexpr int kMaxAB = kStageBytes > kEpArrBytes ? kStageBytes : kEpArrBytes;
 constexpr int kArrBytes = kMaxAB > kTArrBytes ? kMaxAB : kTArrBytes;
 static_assert(kRowBytes == 128 || kRowBytes == 64, "row bytes per stage");
 static_assert(kStages == 2 || kStages == 4, "stage count (the epilogue splits 256 columns)");
 static_assert(kStages * kArrBytes <= 160 * 1024, "LDS budget");
+static_assert(kT == 256 || (kT == 128 && kStages == 2 && kStages * kArrBytes <= 80 * 1024),
+              "the 128 x 128 kernel keeps to half the LDS (two workgroups per compute unit)");
+static_assert(kSuper % kWaves == 0, "whole super-blocks per wave");
 static_assert(kInstPerOperand >= 1, "every wave loads part of each operand");
 static_assert(kKPad % (kStages * kRowBytes / 4) == 0 && kKPad % (kStages * kRowBytes / 2) == 0,
               "padded contraction dims must hold whole blocks of stages");
@@ -106,7 +125,13 @@ static_assert(kKPad % (kStages * kRowBytes / 4) == 0 && kKPad % (kStages * kRowB
 // minimum for 8-byte writes; the store pass's reads (16 lanes: 8 T-rows 8 apart, two
 // adjacent chunks) meet 16 distinct groups.
 __device__ __forceinline__ int tile_chunk(int c, int r) {
-  return (((r >> 3) + 2 * ((c >> 4) & 3)) & (kTile / 8 - 1)) * 8;
+  return (((r >> 3) + 2 * ((c >> 4) & 3)) & (kT / 8 - 1)) * 8;
+}
+
+// First tile of a matrix among this kernel's tiles of its kind (lower-triangle or full).
+__device__ __forceinline__ int tile_prefix(const MatDesc& x, bool tri) {
+  if constexpr (kT == 128) return tri ? x.small_prefix[0] : x.small_prefix[1];
+  else return tri ? x.tri_prefix : x.full_prefix;
 }
 
 // Chunk position of 16-byte chunk c in LDS row r is c ^ swz(r) (a bijection on a row).
@@ -253,15 +278,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
     lo = g.first + u / g.tpm;
     t = u % g.tpm;
   } else {
-    const int v = bid - g.tile_begin + (g.tri ? desc[g.first].tri_prefix : desc[g.first].full_prefix);
+    const bool tri = g.tri != 0;
+    const int v = bid - g.tile_begin + tile_prefix(desc[g.first], tri);
     int hi = g.last - 1;
     lo = g.first;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      const int pre = g.tri ? desc[mid].tri_prefix : desc[mid].full_prefix;
-      if (pre <= v) lo = mid; else hi = mid - 1;
+      if (tile_prefix(desc[mid], tri) <= v) lo = mid; else hi = mid - 1;
     }
-    t = v - (g.tri ? desc[lo].tri_prefix : desc[lo].full_prefix);
+    t = v - tile_prefix(desc[lo], tri);
   }
   const MatDesc& d = desc[lo];
 
@@ -274,28 +299,28 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
   const int cols_out = B.rows;
   int ti, tj;
   if (g.tri) {
-    tri_band_decode(t, (rows_out + kTile - 1) / kTile, ti, tj);
+    tri_band_decode(t, (rows_out + kT - 1) / kT, ti, tj);
   } else {
-    full_band_decode(t, (rows_out + kTile - 1) / kTile, (cols_out + kTile - 1) / kTile, ti, tj);
+    full_band_decode(t, (rows_out + kT - 1) / kT, (cols_out + kT - 1) / kT, ti, tj);
   }
-  const int row0 = ti * kTile;
-  const int col0 = tj * kTile;
+  const int row0 = ti * kT;
+  const int col0 = tj * kT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave / kWavesN;   // 0..1: rows [128 wm, 128 wm + 128)
-  const int wn = wave % kWavesN;   // 0..3: cols [64 wn, 64 wn + 64)
+  const int wm = wave / kWavesN;   // 0..1: rows [kWaveRows wm, kWaveRows (wm + 1))
+  const int wn = wave % kWavesN;   // cols [kWaveCols wn, kWaveCols (wn + 1))
   const int lr = lane & 31;
   const int lk = lane >> 5;
-  // In a diagonal tile the waves with rows [0,128) and columns [128,256) lie strictly above
-  // the diagonal: nothing they compute is stored.
-  const bool above = g.tri && ti == tj && wm == 0 && wn >= 2;
+  // In a diagonal tile the waves of the first half of the rows and the second half of the
+  // columns lie strictly above the diagonal: nothing they compute is stored.
+  const bool above = g.tri && ti == tj && wm == 0 && wn >= kWavesN / 2;
   const bool idle = above || ident;
 
-  f32x16 acc[4][kFragN];
+  f32x16 acc[kFragM][kFragN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kFragM; ++i)
 #pragma unroll
     for (int j = 0; j < kFragN; ++j)
 #pragma unroll
@@ -358,14 +383,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
   });
 
   // Fragment rows of this lane (+ 32 i for A, + 32 j for B).
-  const int a_row = wm * 128 + lr;
-  const int b_row = wn * 64 + lr;
+  const int a_row = wm * kWaveRows + lr;
+  const int b_row = wn * kWaveCols + lr;
   constexpr int kKK = kRowBytes / 32;  // MFMA k-blocks per step
   // Fragments of k-block kk (16-byte chunk 2 kk + lk of the lane's rows) from stage st.
   auto load_frags = [&](const char* st, int kk, uint4* fa, uint4* fb) {
     const int c = 2 * kk + lk;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kFragM; ++i) {
       const int r = a_row + 32 * i;
       fa[i] = *reinterpret_cast<const uint4*>(st + r * kRowBytes + ((c ^ swz(r)) << 4));
     }
@@ -390,10 +415,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
     __builtin_amdgcn_iglp_opt(1);
 #pragma unroll
     for (int kk = 0; kk < kKK; ++kk) {
-      uint4 fa[4], fb[kFragN];
+      uint4 fa[kFragM], fb[kFragN];
       load_frags(st, kk, fa, fb);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kFragM; ++i)
 #pragma unroll
         for (int j = 0; j < kFragN; ++j) Mma<S>::step(fa[i], fb[j], acc[i][j]);
     }
@@ -418,13 +443,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
   // A piece of a split tile: unless it is the tile's last to finish, it leaves its partial
   // sums to that one; the last adds them in and stores the tile.
   if (pieces > 1 &&
-      !split_fixup<4, kFragN>(acc, piece, pieces, cnt, slots, kSlotFloats,
+      !split_fixup<kFragM, kFragN>(acc, piece, pieces, cnt, slots, kSlotFloats,
                               split_flags, idle, args.status,
                               args.split_spins))
     return;
 
   // ---- epilogue ------------------------------------------------------------------------
-  // acc[i][j][r] holds tile element (128 wm + 32 i + 8 (r/4) + 4 lk + r%4, 64 wn + 32 j + lr).
+  // acc[i][j][r] holds tile element (kWaveRows wm + 32 i + 8 (r/4) + 4 lk + r%4,
+  // kWaveCols wn + 32 j + lr).
   float alpha = 1.0f;
   if (g.alpha == kAlphaS) alpha = args.scale[lo];
   else if (g.alpha == kAlphaS2) alpha = args.scale[lo] * args.scale[lo];
@@ -454,15 +480,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
       auto stage = [&](auto kc) {
         constexpr int K = decltype(kc)::value;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kFragM; ++i) {
           u32x2 e4[kFragN][4];
           if constexpr (K == kOpPoly || K == kOpAffine) {
 #pragma unroll
             for (int j = 0; j < kFragN; ++j)
 #pragma unroll
               for (int r4 = 0; r4 < 4; ++r4) {
-                const int gi0 = row0 + 128 * wm + 32 * i + 8 * r4 + 4 * lk;
-                const int gj = col0 + 64 * wn + 32 * j + lr;
+                const int gi0 = row0 + kWaveRows * wm + 32 * i + 8 * r4 + 4 * lk;
+                const int gj = col0 + kWaveCols * wn + 32 * j + lr;
                 e4[j][r4] = u32x2{0u, 0u};
                 if (gj < m && gi0 < m) e4[j][r4] = *(gptr<const u32x2>)(E + int64_t(gj) * lde + gi0);
               }
@@ -471,8 +497,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
           for (int j = 0; j < kFragN; ++j)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-              const int lrow = 128 * wm + 32 * i + 8 * r4 + 4 * lk;  // 4 rows lrow .. lrow+3
-              const int lcol = 64 * wn + 32 * j + lr;
+              const int lrow = kWaveRows * wm + 32 * i + 8 * r4 + 4 * lk;  // 4 rows lrow .. lrow+3
+              const int lcol = kWaveCols * wn + 32 * j + lr;
               const int gi0 = row0 + lrow, gj = col0 + lcol;
               uint16_t o[4];
 #pragma unroll
@@ -533,10 +559,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
       const int d_rows = xform ? C.rows : m;
       const int d_cols = xform ? C.kpad : cstore;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const int sblk = wave + kWaves * sb;  // super-block 0 .. 15
-        const int r = 64 * (sblk >> 2) + 8 * (lane >> 3);
-        const int c = 64 * (sblk & 3) + 8 * (lane & 7);
+      for (int sb = 0; sb < kSuper / kWaves; ++sb) {
+        const int sblk = wave + kWaves * sb;  // super-block 0 .. kSuper - 1
+        const int r = 64 * (sblk / (kT / 64)) + 8 * (lane >> 3);
+        const int c = 64 * (sblk % (kT / 64)) + 8 * (lane & 7);
         const int gi = row0 + r, gj = col0 + c;
         if (!xform && gi < gj) continue;
         const bool diag = !xform && gi == gj;
@@ -577,7 +603,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
   }
 
   // fp32 path (the update, and every op of the fp32 kernel): the accumulators are staged in
-  // fp32, one 128-row half at a time, split by column block across the stage arrays.
+  // fp32, one half (kHalf rows) at a time, split by column block across the stage arrays.
   auto ep_at = [&](int rr, int cc) -> float& {
     const int q = cc / kEpW;
     char* base = q == 0 ? lds0 : q == 1 ? lds1 : q == 2 ? lds2 : lds3;
@@ -588,19 +614,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
   // consecutive columns of the transposed output, consecutive lanes on consecutive row
   // chunks.  Full chunks use one 16- or 32-byte access; chunks that cross the diagonal or an
   // edge fall back to single elements.
-  constexpr int kRowChunks = kTile / 8;   // chunks per row of a half (32)
-  constexpr int kColChunks = 128 / 8;     // chunks per column of a half (16)
-  constexpr int kChunksHalf = 128 * kRowChunks;
-  // Accumulators of rows [128 half, 128 half + 128) into the stage arrays.
+  constexpr int kRowChunks = kT / 8;       // chunks per row of a half
+  constexpr int kColChunks = kHalf / 8;    // chunks per column of a half
+  constexpr int kChunksHalf = kHalf * kRowChunks;
+  // Accumulators of rows [kHalf half, kHalf (half + 1)) into the stage arrays.
   auto stage_half = [&](int half) {
     if (wm == half) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kFragM; ++i)
 #pragma unroll
         for (int j = 0; j < kFragN; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            ep_at(32 * i + 8 * (r >> 2) + 4 * lk + (r & 3), 64 * wn + 32 * j + lr) = acc[i][j][r];
+            ep_at(32 * i + 8 * (r >> 2) + 4 * lk + (r & 3), kWaveCols * wn + 32 * j + lr) = acc[i][j][r];
     }
   };
   if (kind == kOpUpdate) {  // W -= eta * alpha * (A B^T)
@@ -623,7 +649,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
         for (int v = 0; v < kBatch; ++v) {
           int rr, cc;
           chunk(b + v, rr, cc);
-          const int gi = row0 + half * 128 + rr, gj = col0 + cc;
+          const int gi = row0 + half * kHalf + rr, gj = col0 + cc;
           if (gi < rows_out && d.wvec && gj + 7 < cols_out) load8<Wt>(Wp + int64_t(gi) * ldc + gj, w[v]);
         }
       };
@@ -640,7 +666,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
           for (int v = 0; v < kBatch; ++v) {
             int rr, cc;
             chunk(b + v, rr, cc);
-            const int gi = row0 + half * 128 + rr, gj = col0 + cc;
+            const int gi = row0 + half * kHalf + rr, gj = col0 + cc;
             if (gi >= rows_out || gj >= cols_out) continue;
             const gptr<Wt> p = Wp + int64_t(gi) * ldc + gj;
             if (d.wvec && gj + 7 < cols_out) {
@@ -662,7 +688,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
     return;
   }
   for (int half = 0; half < 2; ++half) {
-    const int hr0 = row0 + half * 128;  // first row of this half
+    const int hr0 = row0 + half * kHalf;  // first row of this half
     if (!ident) {
       stage_half(half);
       __syncthreads();
@@ -759,8 +785,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
 
 // The launch: workgroups [0, dp_tiles) run whole tiles in the XCD-aware order; with a tail
 // split the next tail_wgs run one piece each of the last tail_tiles tiles (tile_order.h).
+// Registers: two waves per SIMD (256 a lane): the 256 x 256 kernel's 8 waves, or two
+// workgroups of the 128 x 128 kernel's 4 waves on one compute unit.
 template <typename S, bool kBuf>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
+__global__ __launch_bounds__(kThreads, 512 / kThreads) void k_gemm(GemmArgs args) {
   const int w = int(blockIdx.x);
   int t = 0, piece = 0, pieces = 1;
   int32_t* cnt = nullptr;
@@ -794,7 +822,7 @@ int MUON_LAUNCH_GEMM(const GemmArgs& a, int dtype, void* stream) {
   return hipGetLastError();
 }
 
-#ifndef MUON_GEMM_DEEP
+#if !defined(MUON_GEMM_DEEP) && !defined(MUON_GEMM_SMALL)
 // Test hooks for host-side checks of tile_order.h.
 extern "C" int muon_debug_xcd_remap(int total, int* out) {
   for (int w = 0; w < total; ++w) out[w] = xcd_remap(w, total);

@@ -249,6 +249,9 @@ int run_launch(int dev, hipStream_t s, const Plan& plan, const PlanLaunch& L, in
   if (shape == kCfgWide)
     return timed(dev, s, bf ? "gemm_wide_bf16" : "gemm_wide_f32", L.flops, 0.0,
                  [&] { return muon_launch_gemm_wide(a, L.dtype, s); });
+  if (shape == kShapeSmall)
+    return timed(dev, s, bf ? "gemm_small_bf16" : "gemm_small_f32", L.flops, 0.0,
+                 [&] { return muon_launch_gemm_small(a, L.dtype, s); });
   return timed(dev, s, bf ? "gemm_bf16" : "gemm_f32", L.flops, 0.0,
                [&] { return muon_launch_gemm(a, L.dtype, s); });
 }
@@ -775,7 +778,7 @@ int muon_debug_flat_loads(int32_t on) {
 }
 
 int muon_tune_force(int32_t cfg) {
-  if (cfg < -1 || cfg >= kNumCfg) return fail(MUON_EINVAL, "cfg must be -1, 0, 1, 2, 3 or 4");
+  if (cfg < -1 || cfg >= kNumCfg) return fail(MUON_EINVAL, "cfg must be -1 or 0 .. 5");
   std::lock_guard<std::mutex> lock(g_mu);
   g_force_cfg = cfg;
   return MUON_OK;

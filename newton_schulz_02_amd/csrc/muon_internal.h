@@ -16,23 +16,29 @@
 namespace muon {
 
 constexpr int kTile = 256;       // output tile edge of the square-tile MFMA kernel
+constexpr int kSmallTile = 128;  // output tile edge of the small-tile MFMA kernel
 constexpr int kWideM = 256;      // output tile rows of the wide-tile MFMA kernel
 constexpr int kWideN = 384;      // output tile columns of the wide-tile MFMA kernel
 // MFMA kernel configurations (chosen per launch: tuned, or the square one by default):
 // for 0..3, bit 0 is the tile shape (256 x 256 or 256 x 384) and bit 1 the tail split of the
 // launch's last partial round of workgroups (tile_order.h); 4 is the 256 x 256 kernel with a
-// deeper load pipeline (4 LDS stages of 64-byte rows, three k-steps of loads in flight).
+// deeper load pipeline (4 LDS stages of 64-byte rows, three k-steps of loads in flight); 5
+// is the 128 x 128 kernel (4 waves of 64 x 64, two workgroups per compute unit), for
+// launches with few tiles or short contractions.
 enum GemmCfg : int32_t {
   kCfgSquare = 0,
   kCfgWide = 1,
   kCfgSquareSplit = 2,
   kCfgWideSplit = 3,
   kCfgSquareDeep = 4,
-  kNumCfg = 5
+  kCfgSmall = 5,
+  kNumCfg = 6
 };
-constexpr int kNumShapes = 2;
-inline int cfg_shape(int cfg) { return cfg & 1; }
-inline bool cfg_split(int cfg) { return (cfg & 2) != 0; }
+// Tile shapes: 256 x 256 (kCfgSquare), 256 x 384 (kCfgWide), 128 x 128 (kShapeSmall).
+constexpr int kShapeSmall = 2;
+constexpr int kNumShapes = 3;
+inline int cfg_shape(int cfg) { return cfg == kCfgSmall ? kShapeSmall : (cfg & 1); }
+inline bool cfg_split(int cfg) { return cfg == kCfgSquareSplit || cfg == kCfgWideSplit; }
 inline bool cfg_deep(int cfg) { return cfg == kCfgSquareDeep; }
 constexpr int kMaxUnits = 256;   // compute units a split plans for (MI355X: 256)
 constexpr int kSplitUnit = 4;    // split pieces start and end on multiples of 4 k-steps
@@ -101,6 +107,8 @@ struct MatDesc {
   // The same prefixes for the wide-tile kernel: symmetric m x m outputs, full m x n
   // outputs, full n x m outputs (the update of a tall matrix).
   int32_t wide_prefix[3];
+  // For the small-tile kernel: lower-triangle and full tiles.
+  int32_t small_prefix[2];
 };
 
 struct GroupArg {
@@ -177,6 +185,7 @@ int muon_launch_momentum(const muon::MomArgs& a, int dtype, void* stream);
 int muon_launch_norm(const muon::NormArgs& a, void* stream);
 int muon_launch_gemm(const muon::GemmArgs& a, int dtype, void* stream);
 int muon_launch_gemm_deep(const muon::GemmArgs& a, int dtype, void* stream);
+int muon_launch_gemm_small(const muon::GemmArgs& a, int dtype, void* stream);
 int muon_launch_gemm_wide(const muon::GemmArgs& a, int dtype, void* stream);
 int muon_launch_adamw(const muon::AdamArgs& a, void* stream);
 // noalloc.hip: device address of the allocation-free entry point's scratch array on device

@@ -316,7 +316,7 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
 
   // Schedules and tile counts.
   int max_level = -1;
-  int64_t tri = 0, full = 0, mom = 0, wide[3] = {0, 0, 0};
+  int64_t tri = 0, full = 0, mom = 0, wide[3] = {0, 0, 0}, small[2] = {0, 0};
   for (PlanMat& p : plan->mats) {
     std::vector<SOp> sops;
     const int nv = schedule(steps, p.restarts, p.tall, &sops);
@@ -333,6 +333,11 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
     p.wide_tiles[0] = sym_tiles(int(p.m), kWideM, kWideN);
     p.wide_tiles[1] = ceil_div(p.m, kWideM) * ceil_div(p.n, kWideN);
     p.wide_tiles[2] = ceil_div(p.n, kWideM) * ceil_div(p.m, kWideN);
+    {
+      const int64_t ts = ceil_div(p.m, kSmallTile);
+      p.small_tiles[0] = ts * (ts + 1) / 2;
+      p.small_tiles[1] = ts * ceil_div(p.n, kSmallTile);
+    }
     {  // largest operand, with a tile's overhang of rows, below 2^31 bytes
       const int64_t big = std::max(p.m, p.n);
       p.wide_ok = (big + kWideN) * round_up(big, kKPad) * int64_t(p.gsize) < (int64_t(1) << 31);
@@ -349,6 +354,10 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
       p.wide_prefix[k] = wide[k];
       wide[k] += p.wide_tiles[k];
     }
+    for (int k = 0; k < 2; ++k) {
+      p.small_prefix[k] = small[k];
+      small[k] += p.small_tiles[k];
+    }
     p.mom_prefix = mom;
     tri += p.tri_tiles;
     full += p.full_tiles;
@@ -359,7 +368,7 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
     plan->bytes += p.bytes;
   }
   if (tri > INT32_MAX || full > INT32_MAX || mom > INT32_MAX || wide[0] > INT32_MAX ||
-      wide[1] > INT32_MAX || wide[2] > INT32_MAX) {
+      wide[1] > INT32_MAX || wide[2] > INT32_MAX || small[0] > INT32_MAX || small[1] > INT32_MAX) {
     *err = "too many tiles for one call";
     return MUON_EINVAL;
   }
@@ -497,8 +506,9 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
             int64_t tpm = -1;
             for (int i = g.first; i < g.last; ++i) {
               const PlanMat& p = plan->mats[i];
-              const int64_t nt = sh == kCfgSquare ? (g.op.tri ? p.tri_tiles : p.full_tiles)
-                                                  : p.wide_tiles[g.op.tri ? 0 : (a.nm ? 2 : 1)];
+              const int64_t nt = sh == kCfgSquare  ? (g.op.tri ? p.tri_tiles : p.full_tiles)
+                                 : sh == kShapeSmall ? p.small_tiles[g.op.tri ? 0 : 1]
+                                                     : p.wide_tiles[g.op.tri ? 0 : (a.nm ? 2 : 1)];
               tile_runs[sh].push_back({L.tiles_cfg[sh] + nt, op_ksteps(g.op, p)});
               L.tiles_cfg[sh] += nt;
               tpm = (tpm < 0 || tpm == nt) ? nt : 0;
@@ -569,9 +579,9 @@ void plan_splits(Plan* plan, int units) {
     if (cfg < 0 || cfg >= kNumCfg) cfg = kCfgSquare;
     if (cfg_shape(cfg) == kCfgWide && !L.wide_ok) cfg &= ~1;
     // Long fp32 contractions always run split (accuracy: see kF32SplitMinK); the deep
-    // pipeline has no split, so such a launch runs the 256 x 256 split instead.
+    // pipeline and the small tiles have no split, so such a launch runs the 256 x 256 split.
     if (L.dtype == kF32 && int64_t(L.kmin_cfg[cfg_shape(cfg)]) * 32 >= kF32SplitMinK)
-      cfg = cfg_deep(cfg) ? int(kCfgSquareSplit) : (cfg | 2);
+      cfg = (cfg_deep(cfg) || cfg == kCfgSmall) ? int(kCfgSquareSplit) : (cfg | 2);
     if (cfg_split(cfg) && L.split_cfg[cfg_shape(cfg)].mode == kSplitNone) cfg &= ~2;
     L.cfg = cfg;
     const int sh = cfg_shape(cfg);
@@ -646,6 +656,7 @@ void fill_descs(const Plan& plan, const muon_matrix* mats, const muon_hparams* h
     d.tri_prefix = int32_t(p.tri_prefix);
     d.full_prefix = int32_t(p.full_prefix);
     for (int k = 0; k < 3; ++k) d.wide_prefix[k] = int32_t(p.wide_prefix[k]);
+    for (int k = 0; k < 2; ++k) d.small_prefix[k] = int32_t(p.small_prefix[k]);
     d.eta = float(double(hp->lr) * std::sqrt(std::max(1.0, double(p.r) / double(p.c))));
   }
 }
@@ -696,8 +707,8 @@ std::string describe_plan(const Plan& plan) {
     os << (i ? "," : "") << "{\"kind\":\"" << kLaunch[L.kind] << "\",\"dtype\":" << L.dtype
        << ",\"level\":" << L.level << ",\"tiles\":" << L.tiles << ",\"cfg\":" << L.cfg
        << ",\"grid\":" << L.grid
-       << ",\"tiles_cfg\":[" << L.tiles_cfg[0] << "," << L.tiles_cfg[1] << "]"
-       << ",\"kmin_cfg\":[" << L.kmin_cfg[0] << "," << L.kmin_cfg[1] << "]"
+       << ",\"tiles_cfg\":[" << L.tiles_cfg[0] << "," << L.tiles_cfg[1] << "," << L.tiles_cfg[2] << "]"
+       << ",\"kmin_cfg\":[" << L.kmin_cfg[0] << "," << L.kmin_cfg[1] << "," << L.kmin_cfg[2] << "]"
        << ",\"split_cfg\":[";
     for (int sh = 0; sh < kNumShapes; ++sh) {
       const SplitPlan& sp = L.split_cfg[sh];

@@ -40,6 +40,8 @@ struct PlanMat {
   // Wide-tile kernel: tiles of a symmetric m x m, a full m x n and a full n x m output, and
   // their prefixes over the sorted order.
   int64_t wide_tiles[3] = {0, 0, 0}, wide_prefix[3] = {0, 0, 0};
+  // Small-tile kernel: tiles of a symmetric m x m and of a full m x n output, and prefixes.
+  int64_t small_tiles[2] = {0, 0}, small_prefix[2] = {0, 0};
   bool wide_ok = true;  // every operand fits the 256 x 384 kernel's 32-bit buffer offsets
   bool buf_ok = true;   // every operand (rows x leading dimension) is below 2 GB
   double flops = 0, bytes = 0;
@@ -65,8 +67,8 @@ struct PlanLaunch {
   int cfg = kCfgSquare;          // gemm: the chosen MFMA kernel configuration (GemmCfg)
   int64_t grid = 0;              // gemm: workgroups of the chosen configuration
   std::vector<GroupArg> groups_cfg[kNumShapes];  // gemm: the groups under each tile shape
-  int64_t tiles_cfg[kNumShapes] = {0, 0};
-  int kmin_cfg[kNumShapes] = {0, 0};   // gemm: fewest k-steps among the last kMaxUnits tiles
+  int64_t tiles_cfg[kNumShapes] = {0, 0, 0};
+  int kmin_cfg[kNumShapes] = {0, 0, 0};  // gemm: fewest k-steps among the last kMaxUnits tiles
   SplitPlan split_cfg[kNumShapes];     // gemm: tail split under each tile shape
   bool wide_ok = true;           // gemm: the 256 x 384 configuration may run this launch
   bool buf_ok = true;            // gemm: every operand is below 2 GB (32-bit buffer offsets)

@@ -146,7 +146,8 @@ def test_layer_plan_splits():
                 (ref["mode"], ref["dp_tiles"], ref["tail"], ref["tail_wgs"], ref["slots"])
             assert sp["slots"] <= d["split_slots"]
     sym = gemms[1]   # a symmetric level: 952 square tiles, tail of 184 cut once after 48 of 64
-    assert sym["tiles_cfg"] == [952, 672] and sym["kmin_cfg"] == [64, 64]
+    # (7 lower triangles of 16 x 16 square, 11 x 16 wide and 32 x 32 small tiles)
+    assert sym["tiles_cfg"] == [952, 672, 3696] and sym["kmin_cfg"] == [64, 64, 64]
     assert sym["split_cfg"][0]["mode"] == 2 and sym["split_cfg"][0]["n"] == 3
     assert sym["split_cfg"][0]["tail"] == 184
     upd = gemms[-1]  # the update: 2105 wide tiles, tail of 57 cut into 4
@@ -154,19 +155,19 @@ def test_layer_plan_splits():
     assert upd["split_cfg"][1]["c"] == 4
     # The Gram formation of the wide matrices contracts over 11008; its tail tiles are the
     # square matrices' (4096).
-    assert gemms[0]["kmin_cfg"] == [64, 64]
+    assert gemms[0]["kmin_cfg"] == [64, 64, 64]
 
 
 def test_kmin_is_the_tail_tiles_contraction():
     # fp32: 128 bytes hold 32 elements per k-step; a 1024 x 1024 Gram product has 32 k-steps.
     _, gemms = _gemms([(1024, 1024)], dtype=nm.MUON_F32)
-    assert all(L["kmin_cfg"] == [32, 32] for L in gemms if L["signature"].startswith("f32|2"))
+    assert all(L["kmin_cfg"] == [32, 32, 32] for L in gemms if L["signature"].startswith("f32|2"))
     # bf16 ragged: m = 1100 pads to 1152, 18 k-steps (not a multiple of 4): at most 2 equal
     # pieces of at least 2 units, the last ending at 18.
     _, gemms = _gemms([(1100, 1500)])
     for L in gemms:
         if L["signature"].startswith("bf16|2"):
-            assert L["kmin_cfg"] == [18, 18]
+            assert L["kmin_cfg"] == [18, 18, 18]
             assert L["split_cfg"][0]["mode"] == 1 and L["split_cfg"][0]["c"] == 2
 
 

@@ -59,12 +59,14 @@ def _signature_groups(sig):
 
 
 def _expected_tiles(groups):
-    sq = wide = 0
+    sq = wide = small = 0
     for kind, tri, nmflag, m, n, count in groups:
         if tri:
             t = cdiv(m, 256)
             sq += count * t * (t + 1) // 2
             wide += count * len(wide_sym_set(m))
+            t = cdiv(m, 128)
+            small += count * t * (t + 1) // 2
             continue
         # Full outputs are m x n: the restart product Q X and the update (n x m for the update
         # of a transposed tall matrix).
@@ -74,7 +76,8 @@ def _expected_tiles(groups):
             rows, cols = cols, rows
         sq += count * cdiv(rows, 256) * cdiv(cols, 256)
         wide += count * cdiv(rows, WM) * cdiv(cols, WN)
-    return sq, wide
+        small += count * cdiv(rows, 128) * cdiv(cols, 128)
+    return sq, wide, small
 
 
 @pytest.mark.parametrize("shapes", [
@@ -82,7 +85,7 @@ def _expected_tiles(groups):
     [(4096, 4096)] * 4 + [(4096, 11008)] * 2 + [(11008, 4096)],
     [(1000, 700), (700, 1000), (129, 1), (1, 129), (2048, 6000)],
 ])
-def test_tile_counts_of_both_configurations(shapes):
+def test_tile_counts_of_every_tile_shape(shapes):
     arr = nm.shape_array(shapes)
     d = nm.plan_describe(arr, len(shapes), nm.make_hparams())
     gemms = [L for L in d["launches"] if L["kind"] == "gemm"]
@@ -151,6 +154,20 @@ def test_table_and_force_select_the_configuration(clean_table):
     assert [c for _, c, _, _ in _cfgs(shapes)] == [1 if s == sig else 0 for s, *_ in base]
 
 
+def test_forced_small_tiles(clean_table):
+    """Configuration 5 runs every launch on 128 x 128 tiles, except fp32 launches whose tail
+    tiles contract over 2^17 elements or more: those keep the 256 x 256 tail split."""
+    shapes = [(640, 640), (300, 100), (1000, 700), (129, 1)]
+    nm.tune_force(nm.CFG_SMALL)
+    for s, c, tiles, tcfg in _cfgs(shapes):
+        assert c == nm.CFG_SMALL and tiles == tcfg[2], s
+    d = nm.plan_describe(nm.shape_array([(1024, 1 << 17, nm.MUON_F32)]), 1, nm.make_hparams())
+    syrk = d["launches"][2]
+    assert syrk["cfg"] == nm.CFG_SQUARE_SPLIT and syrk["tiles"] == syrk["tiles_cfg"][0]
+    others = [L for L in d["launches"][3:] if L["kind"] == "gemm"]
+    assert others and all(L["cfg"] == nm.CFG_SMALL for L in others)
+
+
 def test_export_import_round_trip(clean_table):
     head = f"# muon-tune {nm.kernel_hash()}\n"
     assert nm.tune_export() == head
@@ -169,7 +186,7 @@ def test_export_import_round_trip(clean_table):
     assert nm.tune_table()["bf16|0:1:0:640x640*1"] == 0
 
 
-@pytest.mark.parametrize("bad", ["sig", "sig 5", "sig -1", " 1", "a b 1", "sig 1x", "sig ", "sig 12"])
+@pytest.mark.parametrize("bad", ["sig", "sig 6", "sig -1", " 1", "a b 1", "sig 1x", "sig ", "sig 12"])
 def test_malformed_import_adds_nothing(clean_table, bad):
     nm.tune_import("keep 1\n")
     with pytest.raises(nm.MuonError):
@@ -178,7 +195,7 @@ def test_malformed_import_adds_nothing(clean_table, bad):
 
 
 def test_argument_errors(clean_table):
-    for cfg in (-2, 5, 7):
+    for cfg in (-2, 6, 7):
         with pytest.raises(nm.MuonError):
             nm.tune_force(cfg)
     hp = nm.make_hparams()
