@@ -47,18 +47,23 @@ using namespace muon;
 // The library builds this file three times: the 256 x 256 kernel with 2 stages of 128-byte
 // rows (muon_launch_gemm); with MUON_GEMM_DEEP 4 stages of 64-byte rows, three k-steps of
 // loads in flight instead of one (muon_launch_gemm_deep, the deep-pipeline configuration);
-// and with MUON_GEMM_SMALL 128 x 128 tiles run by 4 waves of 64 x 64, whose 64 KB of LDS
-// let two workgroups share a compute unit, one's epilogue overlapping the other's
-// contraction (muon_launch_gemm_small, for launches with few tiles or short contractions).
+// and with MUON_GEMM_SMALL 128 x 128 tiles run by 4 waves of 64 x 64 with 2 stages of
+// 64-byte rows, whose 35 KB of LDS and at most 168 registers a lane let three workgroups
+// share a compute unit, one's epilogue overlapping the others' contractions
+// (muon_launch_gemm_small, for launches with few tiles or short contractions).
 #ifdef MUON_GEMM_DEEP
 #define MUON_GEMM_STAGES 4
 #define MUON_GEMM_ROW_BYTES 64
 #define MUON_LAUNCH_GEMM muon_launch_gemm_deep
+#define MUON_GEMM_KERNEL k_gemm_deep
 #elif defined(MUON_GEMM_SMALL)
 #define MUON_GEMM_TILE 128
+#define MUON_GEMM_ROW_BYTES 64
 #define MUON_LAUNCH_GEMM muon_launch_gemm_small
+#define MUON_GEMM_KERNEL k_gemm_small
 #else
 #define MUON_LAUNCH_GEMM muon_launch_gemm
+#define MUON_GEMM_KERNEL k_gemm
 #endif
 #ifndef MUON_GEMM_TILE
 #define MUON_GEMM_TILE 256
@@ -111,8 +116,8 @@ constexpr int kArrBytes = kMaxAB > kTArrBytes ? kMaxAB : kTArrBytes;
 static_assert(kRowBytes == 128 || kRowBytes == 64, "row bytes per stage");
 static_assert(kStages == 2 || kStages == 4, "stage count (the epilogue splits 256 columns)");
 static_assert(kStages * kArrBytes <= 160 * 1024, "LDS budget");
-static_assert(kT == 256 || (kT == 128 && kStages == 2 && kStages * kArrBytes <= 80 * 1024),
-              "the 128 x 128 kernel keeps to half the LDS (two workgroups per compute unit)");
+static_assert(kT == 256 || (kT == 128 && kStages == 2 && 3 * (kStages * kArrBytes + 1024) <= 160 * 1024),
+              "the 128 x 128 kernel keeps to a third of the LDS (three workgroups per compute unit)");
 static_assert(kSuper % kWaves == 0, "whole super-blocks per wave");
 static_assert(kInstPerOperand >= 1, "every wave loads part of each operand");
 static_assert(kKPad % (kStages * kRowBytes / 4) == 0 && kKPad % (kStages * kRowBytes / 2) == 0,
@@ -785,10 +790,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const int bid, c
 
 // The launch: workgroups [0, dp_tiles) run whole tiles in the XCD-aware order; with a tail
 // split the next tail_wgs run one piece each of the last tail_tiles tiles (tile_order.h).
-// Registers: two waves per SIMD (256 a lane): the 256 x 256 kernel's 8 waves, or two
-// workgroups of the 128 x 128 kernel's 4 waves on one compute unit.
+// Registers: the 256 x 256 kernel's 8 waves run two per SIMD (256 a lane); three workgroups
+// of the 128 x 128 kernel's 4 waves run three per SIMD (168 a lane).
 template <typename S, bool kBuf>
-__global__ __launch_bounds__(kThreads, 512 / kThreads) void k_gemm(GemmArgs args) {
+__global__ __launch_bounds__(kThreads, kT == 256 ? 1 : 3) void MUON_GEMM_KERNEL(GemmArgs args) {
   const int w = int(blockIdx.x);
   int t = 0, piece = 0, pieces = 1;
   int32_t* cnt = nullptr;
@@ -812,13 +817,13 @@ int MUON_LAUNCH_GEMM(const GemmArgs& a, int dtype, void* stream) {
   if (a.grid <= 0) return hipSuccess;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == kBF16 && a.buf32)
-    hipLaunchKernelGGL((k_gemm<uint16_t, true>), dim3(a.grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((MUON_GEMM_KERNEL<uint16_t, true>), dim3(a.grid), dim3(kThreads), 0, s, a);
   else if (dtype == kBF16)
-    hipLaunchKernelGGL((k_gemm<uint16_t, false>), dim3(a.grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((MUON_GEMM_KERNEL<uint16_t, false>), dim3(a.grid), dim3(kThreads), 0, s, a);
   else if (a.buf32)
-    hipLaunchKernelGGL((k_gemm<float, true>), dim3(a.grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((MUON_GEMM_KERNEL<float, true>), dim3(a.grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((k_gemm<float, false>), dim3(a.grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((MUON_GEMM_KERNEL<float, false>), dim3(a.grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
