@@ -246,7 +246,8 @@ def tune_raw(arr, count: int, hp: muon_hparams, ws_ptr: int, ws_bytes: int, scra
 
 
 # MFMA kernel configurations: 256 x 256 and 256 x 384 tiles, each also with the tail split,
-# and the 256 x 256 kernel with the deeper load pipeline (4 LDS stages of 64-byte rows).
+# the 256 x 256 kernel with the deeper load pipeline (4 LDS stages of 64-byte rows), and
+# 128 x 128 tiles (4 waves, three workgroups per compute unit).
 CFG_SQUARE, CFG_WIDE, CFG_SQUARE_SPLIT, CFG_WIDE_SPLIT, CFG_SQUARE_DEEP, CFG_SMALL = 0, 1, 2, 3, 4, 5
 CFG_LABELS = {0: "256x256", 1: "256x384", 2: "256x256+split", 3: "256x384+split", 4: "256x256 deep",
               5: "128x128"}
