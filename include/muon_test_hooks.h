@@ -35,8 +35,9 @@ int muon_debug_wide_tile_order(int tri, int rows, int cols, int* ti, int* tj);
  * range [k0, k1), or -1 in the first field for a workgroup without a piece.  Returns the
  * number of tail workgroups, or MUON_EINVAL for a NULL plan or negative sizes. */
 int muon_debug_split(int tiles, int units, int ksteps, int* plan, int* items, int max_items);
-/* muon_debug_flat_loads: on != 0 makes every later 256 x 256 MFMA launch (of muon_step and
- * shampoo_step) address its operands with 64-bit pointers, the path it otherwise takes only
+/* muon_debug_flat_loads: on != 0 makes every later launch of the 256 x 256 MFMA kernel and of
+ * its deep-pipeline and 128 x 128 builds (of muon_step and shampoo_step) address its operands
+ * with 64-bit pointers, the path it otherwise takes only
  * when an operand of the launch is 2 GB or larger (below that it uses 32-bit buffer
  * offsets); 0 restores the default.  Process-wide.  For tests of that path. */
 int muon_debug_flat_loads(int32_t on);

@@ -1,4 +1,5 @@
-"""Both operand-addressing paths of the 256 x 256 MFMA kernel against the oracle.
+"""Both operand-addressing paths of the 256 x 256 MFMA kernel (and of its deep-pipeline and
+128 x 128 builds) against the oracle.
 
 Launches whose operands are all below 2 GB address them with 32-bit buffer offsets; larger
 ones use 64-bit pointers.  ``flat_loads(True)`` forces the second path at parity-test sizes,
@@ -49,6 +50,17 @@ def test_split_parity(flat):
     log(f"loads flat={flat} split")
     nm.tune_force(nm.CFG_SQUARE_SPLIT)
     wl = W.custom("lds", [(1024, 4096)] * 3, seed=9)
+    res = run_gpu(wl)
+    for i in range(3):
+        check_matrix(res, i, wl)
+
+
+@pytest.mark.parametrize("cfg", [nm.CFG_SQUARE_DEEP, nm.CFG_SMALL], ids=["deep", "small"])
+def test_other_builds_parity(flat, cfg):
+    """The deep-pipeline and 128 x 128 builds of the same kernel source, both addressing paths."""
+    log(f"loads flat={flat} cfg={cfg}")
+    nm.tune_force(cfg)
+    wl = W.custom("ldo", [(700, 900), (900, 700), (257, 513)], seed=31)
     res = run_gpu(wl)
     for i in range(3):
         check_matrix(res, i, wl)
