@@ -160,8 +160,9 @@ int muon_owner_assign(const double* cost, int32_t count, int32_t ranks, int64_t 
  * launch with no tail worth cutting runs 2 as 0 and 3 as 1.  Each MFMA launch of a plan has
  * a signature string
  * (dtype, then per shape group its kind, symmetry, orientation and run-length shapes); a
- * process-wide table maps signatures to configurations, and muon_step uses configuration 0
- * for a signature the table does not hold.  The table is shared by all threads and devices.
+ * process-wide table maps signatures to configurations; for a signature the table does not
+ * hold, muon_step uses configuration 5 when the launch has fewer than 64 tiles of 256 x 256
+ * and configuration 0 otherwise.  The table is shared by all threads and devices.
  * Configuration 1 addresses operands with 32-bit offsets: a launch holding a matrix whose
  * larger side d has (d + 384) * (d rounded up to 128) * element size >= 2^31 bytes always
  * runs configuration 0 (or 2), whatever the table or muon_tune_force say.  An fp32 launch
@@ -183,8 +184,9 @@ int muon_owner_assign(const double* cost, int32_t count, int32_t ranks, int64_t 
  *   of that step it times the same launch in `reps` rounds (1 <= reps <= 64), each round
  *   running it once under every configuration that applies to it.  The configuration with
  *   the smallest median time is stored under the launch's signature when its median is at
- *   least 1 % below configuration 0's, else configuration 0.  A set-up call: it synchronises
- *   the stream before returning, after which the scratch is free again.  Arguments and
+ *   least 1 % below that of the launch's untuned default (5 or 0, above), else the default.
+ *   A set-up call: it synchronises the stream before returning, after which the scratch is
+ *   free again.  Arguments and
  *   errors as muon_step, plus MUON_EINVAL for reps outside [1, 64] or a NULL or misaligned
  *   scratch, and MUON_ENOSPC when scratch_bytes is too small (nothing enqueued then).
  * muon_tune_force: cfg in 0 .. 5 forces that configuration for every launch, -1

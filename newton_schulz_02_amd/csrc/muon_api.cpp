@@ -84,7 +84,7 @@ int g_split_spins = kSplitSpins;
 int choose_cfg(const std::string& sig) {
   if (g_force_cfg >= 0) return g_force_cfg;
   auto it = g_tune.find(sig);
-  return it == g_tune.end() ? int(kCfgSquare) : it->second;
+  return it == g_tune.end() ? -1 : it->second;  // -1: the planner's default for the launch
 }
 std::map<int, std::vector<hipEvent_t>> g_event_pool;
 
@@ -530,10 +530,11 @@ int muon_tune(const muon_matrix* mats, int32_t count, const muon_hparams* hp, vo
         med[cfg] = reps % 2 ? t[size_t(reps / 2)] : 0.5f * (t[size_t(reps / 2) - 1] + t[size_t(reps / 2)]);
       }
       if (e == hipSuccess && rc == MUON_OK) {
-        int best = kCfgSquare;
-        for (int cfg = 1; cfg < kNumCfg; ++cfg)
+        const int base = default_cfg(L.tiles_cfg[kCfgSquare]);  // what an untuned step runs
+        int best = base;
+        for (int cfg = 0; cfg < kNumCfg; ++cfg)
           if (valid[cfg] && med[cfg] < med[best]) best = cfg;
-        g_tune[L.signature] = med[best] < (1.0f - kTuneMargin) * med[kCfgSquare] ? best : int(kCfgSquare);
+        g_tune[L.signature] = med[best] < (1.0f - kTuneMargin) * med[base] ? best : base;
       }
     }
     g_prof = prof;

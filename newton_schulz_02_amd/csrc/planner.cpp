@@ -541,7 +541,8 @@ int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, P
           L.kmin_cfg[sh] = kmin == INT_MAX ? 0 : kmin;
         }
         L.signature = sig.str();
-        L.cfg = choose ? (*choose)(L.signature) : kCfgSquare;
+        L.cfg = choose ? (*choose)(L.signature) : -1;
+        if (L.cfg < 0) L.cfg = default_cfg(L.tiles_cfg[kCfgSquare]);
         plan->launches.push_back(L);
       }
     }

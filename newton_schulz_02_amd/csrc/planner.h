@@ -93,12 +93,21 @@ struct Plan {
   double flops = 0, bytes = 0;
 };
 
-// Chooses the MFMA kernel configuration of a launch from its signature (kCfgSquare when
-// there is no entry).
+// Chooses the MFMA kernel configuration of a launch from its signature, or -1 for the default
+// (default_cfg).
 using CfgChooser = std::function<int(const std::string& signature)>;
 
+// Configuration of a launch that no table entry or force names: the 128 x 128 tiles for a
+// launch of fewer than kSmallDefaultTiles tiles of 256 x 256 (measured: a lone 256 x 1024
+// fp32 matrix, 1 to 16 such tiles per launch, runs 2.4 times faster on them; 160 tiles per
+// launch tie, 952 or more run 15 % slower), else the 256 x 256 tiles.
+constexpr int64_t kSmallDefaultTiles = 64;
+inline int default_cfg(int64_t square_tiles) {
+  return square_tiles < kSmallDefaultTiles ? kCfgSmall : kCfgSquare;
+}
+
 // Validate and plan.  Returns MUON_OK or a negative muon_status with *err set.  Without a
-// chooser every launch uses the square-tile kernel.
+// chooser every launch uses its default configuration (default_cfg).
 int build_plan(const muon_matrix* mats, int32_t count, const muon_hparams* hp, Plan* plan,
                std::string* err, const CfgChooser* choose = nullptr);
 

@@ -356,14 +356,20 @@ def test_two_steps_match_oracle():
     assert relf(to64(dm), M2) < 1e-6
 
 
-def test_profile_reports_each_kernel():
+@pytest.mark.parametrize("cfg,name", [(None, "gemm_small_bf16"), (nm.CFG_SQUARE, "gemm_bf16")])
+def test_profile_reports_each_kernel(cfg, name):
+    """Untuned, these launches (under 64 tiles of 256 x 256) run the 128 x 128 kernel."""
     wl = W.custom("prof", [(256, 1024)] * 2, seed=14)
-    nm.profile_begin()
-    run_gpu(wl)
-    stats = nm.profile_end()
+    nm.tune_force(cfg)
+    try:
+        nm.profile_begin()
+        run_gpu(wl)
+        stats = nm.profile_end()
+    finally:
+        nm.tune_force(None)
     assert stats["momentum_bf16"]["launches"] == 1 and stats["norm"]["launches"] == 1
-    assert stats["gemm_bf16"]["launches"] >= 15
-    assert stats["gemm_bf16"]["ms"] > 0 and stats["gemm_bf16"]["flops"] > 0
+    assert stats[name]["launches"] >= 15
+    assert stats[name]["ms"] > 0 and stats[name]["flops"] > 0
 
 
 def test_profile_times_fit_inside_the_step():

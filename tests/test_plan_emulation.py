@@ -99,15 +99,17 @@ def test_launches_cover_every_op_once(shapes, steps, mask):
         if L["kind"] != "gemm":
             continue
         tiles = 0
+        edge = 128 if L["cfg"] == nm.CFG_SMALL else 256   # the groups of the chosen tile shape
+        assert L["cfg"] in (nm.CFG_SQUARE, nm.CFG_SMALL)
         for g in L["groups"]:
             assert g["tiles_begin"] == tiles
             counts = []
             for i in range(g["first"], g["last"]):
                 got.append((i, L["level"], g["kind"]))
                 m, n = mats[i]["m"], mats[i]["n"]
-                t = -(-m // 256)
+                t = -(-m // edge)
                 counts.append(t * (t + 1) // 2 if g["kind"] in ("syrk", "poly", "prod", "ident")
-                              else t * -(-n // 256))
+                              else t * -(-n // edge))
             tiles += sum(counts)
             # tiles per matrix: set exactly when the group's matrices have equal tile counts
             # (the kernels then find a tile's matrix by division instead of a search)

@@ -98,7 +98,10 @@ def test_tile_counts_of_every_tile_shape(shapes):
         assert all((m <= 128) == (dtype == "f32") for *_, m, n, c in groups)
         assert sum(c for *_, c in groups) >= 1
         assert tuple(L["tiles_cfg"]) == _expected_tiles(groups), L["signature"]
-        assert L["cfg"] == 0 and L["tiles"] == L["tiles_cfg"][0] and L["grid"] == L["tiles"]
+        # untuned default: 128 x 128 tiles below 64 tiles of 256 x 256, else 256 x 256
+        cfg = nm.CFG_SMALL if L["tiles_cfg"][0] < 64 else nm.CFG_SQUARE
+        assert L["cfg"] == cfg and L["tiles"] == L["tiles_cfg"][2 if cfg == nm.CFG_SMALL else 0]
+        assert L["grid"] == L["tiles"]
 
 
 def test_nm_flag_marks_the_transposed_tall_update():
@@ -135,23 +138,29 @@ def _cfgs(shapes):
             if L["kind"] == "gemm"]
 
 
+def _default(tcfg):
+    return nm.CFG_SMALL if tcfg[0] < 64 else nm.CFG_SQUARE
+
+
 def test_table_and_force_select_the_configuration(clean_table):
-    shapes = [(640, 640), (300, 100)]
+    shapes = [(640, 640), (300, 100), (4096, 4096)]
     base = _cfgs(shapes)
-    assert all(c == 0 for _, c, _, _ in base)
+    # Without a table entry a launch of fewer than 64 tiles of 256 x 256 runs 128 x 128 tiles.
+    assert all(c == _default(tcfg) for _, c, _, tcfg in base)
+    assert {c for _, c, _, _ in base} == {nm.CFG_SQUARE, nm.CFG_SMALL}
     # One signature to the wide configuration: only launches with that signature change.
     sig = base[0][0]
     nm.tune_import(f"{sig} 1\n")
     assert nm.tune_table() == {sig: 1}
     for s, c, tiles, tcfg in _cfgs(shapes):
-        assert c == (1 if s == sig else 0)
-        assert tiles == tcfg[c & 1]
+        assert c == (1 if s == sig else _default(tcfg))
+        assert tiles == tcfg[{0: 0, 1: 1, 5: 2}[c]]
     nm.tune_force(nm.CFG_WIDE)
     assert all(c == 1 for _, c, _, _ in _cfgs(shapes))
     nm.tune_force(nm.CFG_SQUARE)
     assert all(c == 0 for _, c, _, _ in _cfgs(shapes))
     nm.tune_force(None)
-    assert [c for _, c, _, _ in _cfgs(shapes)] == [1 if s == sig else 0 for s, *_ in base]
+    assert [c for _, c, _, _ in _cfgs(shapes)] == [1 if s == sig else _default(t) for s, _, _, t in base]
 
 
 def test_forced_small_tiles(clean_table):
